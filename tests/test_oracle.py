@@ -1,0 +1,529 @@
+"""Pins for the fp64 oracle: closed forms, invariants, library cross-checks and
+pure-Python brute force, plus planted mistakes that each pin must catch.
+
+Nothing here needs a GPU. The pins are chosen so that a plausible slip
+anywhere in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a missing normalisation) fails at least one of them; the ``mutant``
+tests plant exactly such slips in copies of the oracle and assert that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle as O
+import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NEG_INF = -math.inf
+
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "closed_forms.json")) as f:
+        g = json.load(f)
+
+    def conv(v):
+        if isinstance(v, list):
+            return [conv(x) for x in v]
+        if v == "-inf":
+            return NEG_INF
+        return v
+    return {k: [{kk: conv(vv) for kk, vv in case.items()} for case in cases]
+            for k, cases in g.items() if not k.startswith("_")}
+
+
+GOLD = _golden()
+
+
+# ---------------------------------------------------------------------------
+# pin predicates: each takes an implementation and says whether it holds
+# ---------------------------------------------------------------------------
+
+def pin_softmax_sums_to_one(softmax_fn):
+    r = np.random.default_rng(11)
+    x = r.normal(0, 3, size=(16, 1000)) + r.uniform(-50, 50, size=(16, 1))
+    y = softmax_fn(x)
+    return bool(np.all(np.isfinite(y)) and np.max(np.abs(y.sum(-1) - 1)) < 1e-13)
+
+
+def pin_softmax_shift_invariance(softmax_fn):
+    r = np.random.default_rng(12)
+    x = r.normal(0, 2, size=(8, 257))
+    base = softmax_fn(x)
+    for c in (50.0, -50.0, 1000.0, -1000.0):
+        y = softmax_fn(x + c)
+        if not np.all(np.isfinite(y)) or np.max(np.abs(y - base)) > 1e-12:
+            return False
+    return True
+
+
+def pin_softmax_golden(softmax_fn):
+    return all(np.allclose(softmax_fn(np.array([c["x"]]))[0], c["y"], rtol=0, atol=1e-15)
+               for c in GOLD["softmax"])
+
+
+def _vis_fn(Lq, Lk, causal, bm, tile):
+    def visible(i, j):
+        ok = True
+        if causal:
+            ok = ok and (j <= i + (Lk - Lq))   # bottom-right aligned causal reading
+        if bm is not None:
+            ok = ok and bm[i // tile][j // tile] != 0
+        return ok
+    return visible
+
+
+def brute_attention(q, k, v, scale, visible):
+    """Pure-Python loops with math.exp / math.fsum; no NumPy arithmetic."""
+    Lq, d = len(q), len(q[0])
+    Lk, dv = len(k), len(v[0])
+    out, lses = [], []
+    for i in range(Lq):
+        keys = [j for j in range(Lk) if visible(i, j)]
+        if not keys:
+            out.append([0.0] * dv)
+            lses.append(NEG_INF)
+            continue
+        s = {j: scale * math.fsum(q[i][e] * k[j][e] for e in range(d)) for j in keys}
+        mx = max(s.values())
+        ex = {j: math.exp(s[j] - mx) for j in keys}
+        den = math.fsum(ex.values())
+        out.append([math.fsum(ex[j] * v[j][e] for j in keys) / den for e in range(dv)])
+        lses.append(mx + math.log(den))
+    return out, lses
+
+
+BRUTE_CASES = [
+    # (Lq, Lk, d, dv, causal, block mask (tile 2) or None, scale)
+    (4, 4, 4, 4, False, None, 0.5),
+    (4, 4, 4, 4, True, None, 0.5),
+    (3, 5, 4, 2, True, None, 0.7),                      # Lq != Lk: bottom-right alignment
+    (4, 4, 4, 4, False, [[1, 0], [1, 1]], 0.5),
+    (4, 6, 3, 4, True, [[0, 1, 1], [1, 0, 1]], 1.3),
+    (4, 4, 4, 4, True, [[0, 0], [1, 1]], 0.5),          # rows 0-1 have no visible key
+    (1, 7, 4, 4, True, None, 0.5),                      # decode-shaped
+]
+
+
+def pin_attention_bruteforce(attn_fn):
+    r = np.random.default_rng(13)
+    for (Lq, Lk, d, dv, causal, bm, scale) in BRUTE_CASES:
+        q = r.normal(size=(1, 1, Lq, d))
+        k = r.normal(size=(1, 1, Lk, d))
+        v = r.normal(size=(1, 1, Lk, dv))
+        bmm = None if bm is None else np.array(bm, dtype=np.uint8)
+        o, lse = attn_fn(q, k, v, scale, causal, bmm, 2)
+        bo, blse = brute_attention(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), scale,
+                                   _vis_fn(Lq, Lk, causal, bm, 2))
+        if not np.allclose(o[0, 0], np.array(bo), rtol=0, atol=1e-13):
+            return False
+        bl = np.array(blse)
+        fin = np.isfinite(bl)
+        if not np.array_equal(fin, np.isfinite(lse[0, 0])):
+            return False
+        if not np.allclose(lse[0, 0][fin], bl[fin], rtol=0, atol=1e-13):
+            return False
+        if np.any(lse[0, 0][~fin] != NEG_INF):
+            return False
+    return True
+
+
+def pin_attention_uniform_query(attn_fn):
+    """q = 0: every visible key gets the same weight, so O is the mean of the
+    visible V rows and LSE = ln(number of visible keys)."""
+    r = np.random.default_rng(14)
+    for (Lq, Lk, causal) in [(6, 6, True), (3, 9, True), (5, 5, False)]:
+        q = np.zeros((1, 1, Lq, 8))
+        k = r.normal(size=(1, 1, Lk, 8))
+        v = r.normal(size=(1, 1, Lk, 3))
+        o, lse = attn_fn(q, k, v, 0.3, causal, None, 64)
+        for i in range(Lq):
+            n = (i + 1 + Lk - Lq) if causal else Lk
+            if abs(lse[0, 0, i] - math.log(n)) > 1e-13:
+                return False
+            if not np.allclose(o[0, 0, i], v[0, 0, :n].mean(0), rtol=0, atol=1e-13):
+                return False
+    return True
+
+
+def pin_attention_identity_values(attn_fn):
+    """V = I (Lk = d): O is the softmax matrix itself; compare with SciPy."""
+    r = np.random.default_rng(15)
+    q = r.normal(size=(2, 2, 5, 6))
+    k = r.normal(size=(2, 2, 6, 6))
+    v = np.broadcast_to(np.eye(6), (2, 2, 6, 6)).copy()
+    o, lse = attn_fn(q, k, v, 0.4, False, None, 64)
+    s = 0.4 * np.einsum("bhqd,bhkd->bhqk", q, k)
+    return bool(np.allclose(o, scipy.special.softmax(s, axis=-1), rtol=0, atol=1e-14)
+                and np.allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=0, atol=1e-13))
+
+
+def pin_attention_single_key(attn_fn):
+    """Lk = 1: O = v_0 and LSE = s_00, exactly; causal row 0 of a square problem likewise."""
+    r = np.random.default_rng(16)
+    q = r.normal(size=(1, 1, 3, 4))
+    k = r.normal(size=(1, 1, 1, 4))
+    v = r.normal(size=(1, 1, 1, 4))
+    o, lse = attn_fn(q, k, v, 0.9, False, None, 64)
+    if not np.array_equal(o[0, 0], np.repeat(v[0, 0], 3, axis=0)):
+        return False
+    if not np.allclose(lse[0, 0], 0.9 * (q[0, 0] @ k[0, 0, 0]), rtol=0, atol=1e-15):
+        return False
+    k2 = r.normal(size=(1, 1, 3, 4))
+    v2 = r.normal(size=(1, 1, 3, 4))
+    o2, lse2 = attn_fn(q, k2, v2, 0.9, True, None, 64)
+    return bool(np.array_equal(o2[0, 0, 0], v2[0, 0, 0])
+                and abs(lse2[0, 0, 0] - 0.9 * q[0, 0, 0] @ k2[0, 0, 0]) < 1e-15)
+
+
+def pin_attention_key_permutation(attn_fn):
+    """Without a mask, permuting keys together with their values changes nothing."""
+    r = np.random.default_rng(17)
+    q = r.normal(size=(1, 2, 4, 5))
+    k = r.normal(size=(1, 2, 9, 5))
+    v = r.normal(size=(1, 2, 9, 3))
+    perm = r.permutation(9)
+    o1, l1 = attn_fn(q, k, v, 0.6, False, None, 64)
+    o2, l2 = attn_fn(q, k[:, :, perm], v[:, :, perm], 0.6, False, None, 64)
+    return bool(np.allclose(o1, o2, rtol=0, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-14))
+
+
+def pin_merge_golden(merge_fn):
+    for c in GOLD["lse_merge"]:
+        o, lse = merge_fn(np.array(c["o_parts"]), np.array(c["lse_parts"]))
+        if not np.allclose(o, c["o"], rtol=0, atol=1e-15):
+            return False
+        if c["lse"] == NEG_INF:
+            if lse != NEG_INF:
+                return False
+        elif abs(lse - c["lse"]) > 1e-15:
+            return False
+    return True
+
+
+def pin_merge_monoid(merge_fn):
+    """Associativity, commutativity, identity, at lse magnitudes where exp overflows."""
+    r = np.random.default_rng(18)
+    for offset in (0.0, 800.0, -800.0):
+        parts = [(r.normal(size=4), r.normal() * 5 + offset) for _ in range(3)]
+
+        def m2(a, b):
+            o, l = merge_fn(np.stack([a[0], b[0]]), np.array([a[1], b[1]]))
+            return (o, float(l))
+        ab_c = m2(m2(parts[0], parts[1]), parts[2])
+        a_bc = m2(parts[0], m2(parts[1], parts[2]))
+        flat = merge_fn(np.stack([p[0] for p in parts]), np.array([p[1] for p in parts]))
+        ba = m2(parts[1], parts[0])
+        ab = m2(parts[0], parts[1])
+        ident = m2(parts[0], (np.full(4, np.nan), NEG_INF))
+        for x, y in ((ab_c, a_bc), (ab_c, (flat[0], float(flat[1]))), (ab, ba), (ident, parts[0])):
+            if not (np.all(np.isfinite(x[0])) and np.allclose(x[0], y[0], rtol=0, atol=1e-13)
+                    and abs(x[1] - y[1]) <= 1e-13 * max(1.0, abs(y[1]))):
+                return False
+    return True
+
+
+def pin_split_merge_equals_unsplit(partials_fn, merge_fn, attn_fn):
+    """The multi-segment strategy: split the keys, attend per chunk, merge == unsplit."""
+    r = np.random.default_rng(19)
+    for (Lk, S) in [(37, 4), (5, 8), (64, 1), (100, 7)]:      # includes empty chunks
+        q = r.normal(size=(2, 3, 1, 8))
+        k = r.normal(size=(2, 3, Lk, 8))
+        v = r.normal(size=(2, 3, Lk, 6))
+        op, lp = partials_fn(q, k, v, 0.35, S)
+        o, lse = merge_fn(op, lp)
+        ref_o, ref_lse = attn_fn(q, k, v, 0.35, False, None, 64)
+        if not (np.allclose(o, ref_o[:, :, 0], rtol=0, atol=1e-13)
+                and np.allclose(lse, ref_lse[:, :, 0], rtol=0, atol=1e-12)):
+            return False
+    return True
+
+
+# ---------------------------------------------------------------------------
+# the oracle satisfies every pin
+# ---------------------------------------------------------------------------
+
+def _oracle_attn(q, k, v, scale, causal, bm, tile):
+    return O.attention(q, k, v, scale, causal, bm, tile)
+
+
+def test_softmax_pins():
+    assert pin_softmax_sums_to_one(O.softmax_rows)
+    assert pin_softmax_shift_invariance(O.softmax_rows)
+    assert pin_softmax_golden(O.softmax_rows)
+
+
+def test_softmax_naive_form_overflows():
+    """The +1000 shift pin has teeth: the unshifted exp overflows even in fp64."""
+    x = np.array([[1000.0, 999.0, 998.0]])
+    with np.errstate(over="ignore", invalid="ignore"):
+        naive = np.exp(x) / np.exp(x).sum(-1, keepdims=True)
+    assert np.isnan(naive).all()
+    assert np.allclose(O.softmax_rows(x), scipy.special.softmax(x, axis=-1), rtol=0, atol=1e-15)
+
+
+def test_softmax_vs_scipy_on_workload_rows():
+    x = W.softmax_rows_input(2, 6, 32768)
+    ref = scipy.special.softmax(x.astype(np.float64), axis=-1)
+    assert np.max(np.abs(O.softmax_rows(x) - ref)) < 1e-14
+
+
+def test_logsumexp_golden_and_scipy():
+    for c in GOLD["logsumexp"]:
+        assert abs(O.logsumexp_rows(np.array(c["x"])) - c["lse"]) < 1e-13
+    r = np.random.default_rng(3)
+    x = r.normal(0, 10, size=(5, 77))
+    assert np.allclose(O.logsumexp_rows(x), scipy.special.logsumexp(x, axis=-1), rtol=0, atol=1e-12)
+    assert O.logsumexp_rows(np.array([NEG_INF, NEG_INF])) == NEG_INF
+
+
+@pytest.mark.parametrize("tile", [1, 7, 64, 1000, 5000])
+def test_online_stats_equal_three_pass(tile):
+    r = np.random.default_rng(tile)
+    x = r.normal(0, 2, 1000) + r.uniform(-50, 50)
+    # make the running max change in almost every tile (monotone ramp)
+    x[::3] += np.linspace(0, 30, len(x[::3]))
+    m, l = O.online_softmax_stats(x, tile)
+    assert m == x.max()
+    ref_l = np.exp(x - x.max()).sum()
+    assert abs(l - ref_l) <= 1e-12 * ref_l
+
+
+@pytest.mark.parametrize("tile", [1, 7, 64, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_attention_equals_three_pass(tile, causal):
+    r = np.random.default_rng(100 + tile)
+    Lq, Lk, d = 5, 300, 16
+    q = r.normal(size=(1, 1, Lq, d))
+    k = r.normal(size=(1, 1, Lk, d)) + np.linspace(0, 3, Lk)[:, None]   # rising scores
+    v = r.normal(size=(1, 1, Lk, 8))
+    bm = (r.uniform(size=(1, 5)) < 0.6).astype(np.uint8)
+    bm[0, 0] = 1
+    ref_o, ref_lse = O.attention(q, k, v, 0.25, causal, bm, 64)
+    vis = O.element_mask(Lq, Lk, causal, bm, 64)
+    for i in range(Lq):
+        o, lse = O.online_attention(q[0, 0, i], k[0, 0], v[0, 0], 0.25, tile, vis[i])
+        assert np.allclose(o, ref_o[0, 0, i], rtol=1e-12, atol=1e-13)
+        assert abs(lse - ref_lse[0, 0, i]) <= 1e-12 * max(1, abs(lse))
+
+
+def test_attention_pins():
+    assert pin_attention_bruteforce(_oracle_attn)
+    assert pin_attention_uniform_query(_oracle_attn)
+    assert pin_attention_identity_values(_oracle_attn)
+    assert pin_attention_single_key(_oracle_attn)
+    assert pin_attention_key_permutation(_oracle_attn)
+
+
+def test_fully_masked_rows_and_empty_keys():
+    r = np.random.default_rng(4)
+    q = r.normal(size=(1, 1, 4, 4))
+    k = r.normal(size=(1, 1, 4, 4))
+    v = r.normal(size=(1, 1, 4, 4))
+    bm = np.array([[0]], dtype=np.uint8)
+    o, lse = O.attention(q, k, v, 0.5, False, bm, 64)
+    assert np.array_equal(o, np.zeros_like(o)) and np.all(lse == NEG_INF)
+    o, lse = O.attention(q, k[:, :, :0], v[:, :, :0], 0.5, False)
+    assert np.array_equal(o, np.zeros((1, 1, 4, 4))) and np.all(lse == NEG_INF)
+
+
+def test_causal_single_query_sees_every_key():
+    """Bottom-right alignment: a one-row query attends its whole key range."""
+    r = np.random.default_rng(5)
+    q = r.normal(size=(2, 2, 1, 8))
+    k = r.normal(size=(2, 2, 50, 8))
+    v = r.normal(size=(2, 2, 50, 8))
+    a = O.attention(q, k, v, 0.3, True)
+    b = O.attention(q, k, v, 0.3, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_q_rows_subset_matches_full():
+    r = np.random.default_rng(6)
+    q = r.normal(size=(1, 2, 130, 8))
+    k = r.normal(size=(1, 2, 140, 8))
+    v = r.normal(size=(1, 2, 140, 8))
+    bm = (r.uniform(size=(3, 3)) < 0.5).astype(np.uint8)
+    full = O.attention(q, k, v, 0.3, True, bm)
+    rows = [0, 63, 64, 129]
+    sub = O.attention(q, k, v, 0.3, True, bm, q_rows=rows)
+    assert np.array_equal(sub[0], full[0][:, :, rows]) and np.array_equal(sub[1], full[1][:, :, rows])
+
+
+def test_merge_pins():
+    assert pin_merge_golden(O.lse_merge)
+    assert pin_merge_monoid(O.lse_merge)
+    assert pin_split_merge_equals_unsplit(O.decode_splitkv_partials, O.lse_merge, _oracle_attn)
+
+
+def test_split_ranges():
+    assert O.split_ranges(32768, 16) == [(2048 * s, 2048 * (s + 1)) for s in range(16)]
+    assert O.split_ranges(5, 8) == [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 5), (5, 5), (5, 5)]
+    assert O.split_ranges(0, 3) == [(0, 0)] * 3
+
+
+def test_bf16_widening_known_bits():
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x4049, 0x0000, 0x8000], dtype=np.uint16)
+    want = [1.0, -2.0, math.inf, -math.inf, 2.0 ** -133, 3.140625, 0.0, -0.0]
+    got = O.bf16_bits_to_f64(bits)
+    assert all(g == w for g, w in zip(got.tolist(), want))
+    assert math.copysign(1, got[-1]) == -1
+
+
+def test_bf16_rounding_ties_and_cross_check():
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0, 1 + 2 ** -8 + 2 ** -30])
+    assert O.round_to_bf16(x).tolist() == [1.0, 1 + 2 ** -6, -1.0, 3.0, 1 + 2 ** -7]
+    # two independent implementations agree on float32-representable values
+    r = np.random.default_rng(7)
+    f = (r.normal(size=20000) * np.exp2(r.integers(-20, 20, 20000))).astype(np.float32)
+    via_bits = O.bf16_bits_to_f64(W.f32_to_bf16_bits(f))
+    assert np.array_equal(via_bits, O.round_to_bf16(f.astype(np.float64)))
+
+
+def test_workload_generators_are_pure_functions_of_the_seed():
+    a = W.normal_head(3, W.TID_Q, 1, 2, 16, 8, "bf16")
+    b = W.normal_head(3, W.TID_Q, 1, 2, 16, 8, "bf16")
+    c = W.normal_head(3, W.TID_Q, 1, 3, 16, 8, "bf16")
+    assert a.dtype == np.uint16 and np.array_equal(a, b) and not np.array_equal(a, c)
+    t = W.normal_tensor(3, W.TID_Q, 2, 3, 16, 8, "bf16")
+    assert np.array_equal(t[1, 2], a)
+    x = W.softmax_rows_input(2, 3, 100, row_ids=[5, 9, 5])
+    assert np.array_equal(x[0], x[2]) and np.array_equal(x[0], W.softmax_row(2, 5, 100))
+
+
+def test_config5_mask_counts():
+    m = W.config_block_mask(5)
+    assert m.shape == (128, 128)
+    window = sum(min(i + 1, 8) for i in range(128))
+    assert window == 996
+    assert int(m.sum()) == 996 + 726
+    assert np.all(np.triu(m, 1) == 0)                    # nothing above the diagonal
+    assert np.all(np.diag(m) == 1)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: every mutant must fail at least one pin
+# ---------------------------------------------------------------------------
+
+def _softmax_no_shift(x):
+    e = np.exp(np.asarray(x, np.float64))
+    return e / e.sum(-1, keepdims=True)
+
+
+def _softmax_divides_by_max(x):
+    x = np.asarray(x, np.float64)
+    m = x.max(-1, keepdims=True)
+    return np.exp(x - m) / np.exp(x - m).max(-1, keepdims=True)
+
+
+def _softmax_wrong_sign(x):
+    x = np.asarray(x, np.float64)
+    m = x.max(-1, keepdims=True)
+    return np.exp(m - x) / np.exp(m - x).sum(-1, keepdims=True)
+
+
+@pytest.mark.parametrize("mutant", [_softmax_no_shift, _softmax_divides_by_max, _softmax_wrong_sign])
+def test_softmax_mutants_are_caught(mutant):
+    with np.errstate(all="ignore"):
+        caught = not (pin_softmax_sums_to_one(mutant) and pin_softmax_shift_invariance(mutant)
+                      and pin_softmax_golden(mutant))
+    assert caught
+
+
+def _attn_mutant(kind):
+    def fn(q, k, v, scale, causal, bm, tile):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        B, H, Lq, d = q.shape
+        Lk = k.shape[2]
+        i = np.arange(Lq)[:, None]
+        j = np.arange(Lk)[None, :]
+        vis = np.ones((Lq, Lk), bool)
+        if causal:
+            if kind == "causal_top_left":
+                vis &= j <= i
+            elif kind == "causal_flipped":
+                vis &= j >= i + (Lk - Lq)
+            else:
+                vis &= j <= i + (Lk - Lq)
+        if bm is not None:
+            if kind == "mask_transposed":
+                vis &= np.asarray(bm)[(j // tile) % bm.shape[0], (i // tile) % bm.shape[1]] != 0
+            else:
+                vis &= np.asarray(bm)[i // tile, j // tile] != 0
+        Oo = np.zeros((B, H, Lq, v.shape[3]))
+        L = np.full((B, H, Lq), NEG_INF)
+        for b in range(B):
+            for h in range(H):
+                sc = 1.0 if kind == "no_scale" else scale
+                if kind == "transposed_operand" and Lq == Lk:
+                    S = sc * (k[b, h] @ q[b, h].T)
+                else:
+                    S = sc * (q[b, h] @ k[b, h].T)
+                S = np.where(vis, S, NEG_INF)
+                m = S.max(1)
+                has = np.isfinite(m)
+                ms = np.where(has, m, 0.0)
+                E = np.exp(S - ms[:, None])
+                l = E.sum(1)
+                ls = np.where(has, l, 1.0)
+                P = E if kind == "no_normalise" else E / ls[:, None]
+                Oo[b, h] = P @ v[b, h]
+                Oo[b, h][~has] = 0
+                L[b, h] = np.where(has, (np.log(ls) if kind == "lse_no_max" else ms + np.log(ls)), NEG_INF)
+        return Oo, L
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "transposed_operand", "causal_top_left", "causal_flipped",
+                                  "mask_transposed", "no_normalise", "lse_no_max"])
+def test_attention_mutants_are_caught(kind):
+    fn = _attn_mutant(kind)
+    with np.errstate(all="ignore"):
+        ok = (pin_attention_bruteforce(fn) and pin_attention_uniform_query(fn)
+              and pin_attention_identity_values(fn) and pin_attention_single_key(fn)
+              and pin_attention_key_permutation(fn))
+    assert not ok
+    # the same skeleton without a planted mistake passes (the mutant harness is sound)
+    assert pin_attention_bruteforce(_attn_mutant("none"))
+
+
+def _merge_mutant(kind):
+    def fn(o_parts, lse_parts):
+        o_parts = np.asarray(o_parts, np.float64)
+        lse_parts = np.asarray(lse_parts, np.float64)
+        M = lse_parts.max(-1)
+        has = np.isfinite(M)
+        Ms = np.where(has, M, 0.0)
+        live = np.isfinite(lse_parts)
+        if kind == "no_max_shift":
+            w = np.where(live, np.exp(np.where(live, lse_parts, 0.0)), 0.0)
+        else:
+            w = np.where(live, np.exp(np.where(live, lse_parts, 0.0) - Ms[..., None]), 0.0)
+        Wt = w.sum(-1)
+        c = np.where(live[..., None], w[..., None] * np.where(live[..., None], o_parts, 0.0), 0.0).sum(-2)
+        Ws = np.where(has, Wt, 1.0)
+        Oo = c if kind == "no_divide" else c / Ws[..., None]
+        Oo = np.where(has[..., None], Oo, 0.0)
+        if kind == "lse_no_log":
+            L = np.where(has, Ms + Ws, NEG_INF)
+        elif kind == "no_max_shift":
+            L = np.where(has, np.log(Ws), NEG_INF)
+        else:
+            L = np.where(has, Ms + np.log(Ws), NEG_INF)
+        return Oo, L
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["no_max_shift", "no_divide", "lse_no_log"])
+def test_merge_mutants_are_caught(kind):
+    fn = _merge_mutant(kind)
+    with np.errstate(all="ignore"):
+        ok = (pin_merge_golden(fn) and pin_merge_monoid(fn)
+              and pin_split_merge_equals_unsplit(O.decode_splitkv_partials, fn, _oracle_attn))
+    assert not ok
+    assert pin_merge_golden(_merge_mutant("none")) and pin_merge_monoid(_merge_mutant("none"))

@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs shared by the fp64 oracle and the GPU path.
+
+This module only *draws* inputs. It contains none of the arithmetic of the
+method (no max, no exponential, no normalisation, no contraction): both the
+oracle and the device path consume exactly the arrays produced here, and each
+side interprets them on its own.
+
+Every tensor slice is a pure function of (config seed, tensor id, slice
+index): a NumPy ``Generator(PCG64(SeedSequence([seed, tensor_id, *index])))``
+draws it. So any single attention head, or any single softmax row, can be
+regenerated on any machine without materialising the whole tensor, which is
+what lets the oracle check sampled heads of a 32 GiB decode cache.
+
+Value distributions follow the workloads the pages describe: i.i.d. N(0, 1)
+queries, keys and values; softmax rows of N(0, 2^2) plus a per-row offset
+uniform in [-50, 50]; block masks of the causal / sliding-window / random
+kinds that the STOF page (Accelerating Sparse Transformer Inference on GPU,
+Résumé technique, Énoncé du problème) lists as the sparsity patterns that
+matter.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+# Tensor ids inside one config's seed space.
+TID_Q, TID_K, TID_V, TID_X, TID_MASK, TID_U = 0, 1, 2, 3, 4, 5
+
+MASK_TILE = 64  # granularity of the block mask, in tokens, on both axes
+
+# The five workloads. Sizes are the ones the throughput figures are quoted on.
+CONFIGS = {
+    1: dict(name="attn_f32_B1_H1_L128_d64", kind="attention", dtype="f32",
+            B=1, H=1, Lq=128, Lk=128, d=64, scale=1.0 / math.sqrt(64),
+            causal=False, mask=None),
+    2: dict(name="softmax_f32_4096x32768", kind="softmax", dtype="f32",
+            rows=4096, cols=32768),
+    3: dict(name="causal_prefill_bf16_B4_H32_L4096_d128", kind="attention",
+            dtype="bf16", B=4, H=32, Lq=4096, Lk=4096, d=128,
+            scale=1.0 / math.sqrt(128), causal=True, mask=None),
+    4: dict(name="splitkv_decode_bf16_B64_H32_Lk32768_d128_s16",
+            kind="decode", dtype="bf16", B=64, H=32, Lk=32768, d=128,
+            scale=1.0 / math.sqrt(128), num_splits=16),
+    5: dict(name="block_sparse_bf16_B2_H16_L8192_d64", kind="attention",
+            dtype="bf16", B=2, H=16, Lq=8192, Lk=8192, d=64,
+            scale=1.0 / math.sqrt(64), causal=True, mask="window512_rand10"),
+}
+
+
+def rng(seed: int, tensor_id: int, *index: int) -> np.random.Generator:
+    """The one generator every slice comes from."""
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence([int(seed), int(tensor_id)] + [int(i) for i in index])))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the raw uint16 bits.
+
+    Input preparation only: the draws are float32, the bf16 workloads store
+    the rounded bit patterns, and both sides widen those bits themselves.
+    """
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    out = ((b + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def normal_head(seed: int, tensor_id: int, b: int, h: int, L: int, d: int, dtype: str) -> np.ndarray:
+    """One [L, d] head of i.i.d. N(0, 1): float32, or bf16 bits (uint16) when dtype == 'bf16'."""
+    z = rng(seed, tensor_id, b, h).standard_normal((L, d), dtype=np.float32)
+    return f32_to_bf16_bits(z) if dtype == "bf16" else z
+
+
+def _fill_heads(args):
+    seed, tensor_id, B, H, L, d, dtype, shm_name, lo, hi = args
+    from multiprocessing import shared_memory
+    shm = shared_memory.SharedMemory(name=shm_name)
+    try:
+        npdt = np.uint16 if dtype == "bf16" else np.float32
+        arr = np.ndarray((B * H, L, d), dtype=npdt, buffer=shm.buf)
+        for bh in range(lo, hi):
+            arr[bh] = normal_head(seed, tensor_id, bh // H, bh % H, L, d, dtype)
+        del arr
+    finally:
+        shm.close()
+    return hi - lo
+
+
+def normal_tensor(seed: int, tensor_id: int, B: int, H: int, L: int, d: int, dtype: str,
+                  workers: int | None = None) -> np.ndarray:
+    """A [B, H, L, d] tensor assembled from per-head draws (parallel for large tensors)."""
+    npdt = np.uint16 if dtype == "bf16" else np.float32
+    n_heads = B * H
+    nbytes = n_heads * L * d * np.dtype(npdt).itemsize
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    if nbytes < (256 << 20) or workers <= 1:
+        out = np.empty((n_heads, L, d), dtype=npdt)
+        for bh in range(n_heads):
+            out[bh] = normal_head(seed, tensor_id, bh // H, bh % H, L, d, dtype)
+        return out.reshape(B, H, L, d)
+    from multiprocessing import get_context, shared_memory
+    shm = shared_memory.SharedMemory(create=True, size=nbytes)
+    try:
+        step = max(1, math.ceil(n_heads / (workers * 4)))
+        jobs = [(seed, tensor_id, B, H, L, d, dtype, shm.name, lo, min(n_heads, lo + step))
+                for lo in range(0, n_heads, step)]
+        with ProcessPoolExecutor(max_workers=workers, mp_context=get_context("fork")) as ex:
+            done = sum(ex.map(_fill_heads, jobs))
+        assert done == n_heads
+        view = np.ndarray((B, H, L, d), dtype=npdt, buffer=shm.buf)
+        out = np.empty_like(view)
+        np.copyto(out, view)
+        del view
+        return out
+    finally:
+        shm.close()
+        shm.unlink()
+
+
+def softmax_row(seed: int, r: int, cols: int) -> np.ndarray:
+    """Row r of the softmax workload: float32(2 z + u_r), z ~ N(0, 1), u_r ~ U[-50, 50]."""
+    z = rng(seed, TID_X, r).standard_normal(cols, dtype=np.float32)
+    u = rng(seed, TID_U, r).uniform(-50.0, 50.0)
+    return (2.0 * z.astype(np.float64) + u).astype(np.float32)
+
+
+def softmax_rows_input(seed: int, rows: int, cols: int, row_ids=None) -> np.ndarray:
+    ids = range(rows) if row_ids is None else row_ids
+    return np.stack([softmax_row(seed, int(r), cols) for r in ids]) if len(ids) else \
+        np.zeros((0, cols), np.float32)
+
+
+def window_random_block_mask(seed: int, n_tiles: int, window_tiles: int = 8,
+                             frac: float = 0.10) -> np.ndarray:
+    """uint8 [n_tiles, n_tiles] tile mask: a causal sliding window plus random lower tiles.
+
+    Tile (I, J) is active when I - window_tiles < J <= I (the window, diagonal
+    included), plus exactly round(frac * N) tiles drawn uniformly without
+    replacement from the N tiles strictly below the window (J <= I - window_tiles).
+    """
+    m = np.zeros((n_tiles, n_tiles), dtype=np.uint8)
+    for i in range(n_tiles):
+        m[i, max(0, i - window_tiles + 1): i + 1] = 1
+    cand_i, cand_j = np.nonzero(np.tril(np.ones((n_tiles, n_tiles), bool), k=-window_tiles))
+    n_pick = int(round(frac * len(cand_i)))
+    if n_pick:
+        pick = rng(seed, TID_MASK).choice(len(cand_i), size=n_pick, replace=False)
+        m[cand_i[pick], cand_j[pick]] = 1
+    return m
+
+
+def config_block_mask(cfg: int):
+    c = CONFIGS[cfg]
+    if c.get("mask") != "window512_rand10":
+        return None
+    n = math.ceil(c["Lq"] / MASK_TILE)
+    return window_random_block_mask(cfg, n, window_tiles=512 // MASK_TILE, frac=0.10)
