@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Throughput of the online-softmax attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads softmax,prefill,decode,sparse,attn_f32]
+
+One JSON line is printed. Its headline (``value``) is the row-softmax
+workload, fp32 4096 x 32768, in GB/s of algorithmic HBM traffic (one read and
+one write per element); every workload that ran is also reported under
+``workloads`` with its own time, throughput and roofline: causal bf16 prefill
+(B4 H32 L4096 d128, TFLOP/s), split-KV bf16 decode (B64 H32 Lk32768 d128, 16
+splits, GB/s), block-sparse bf16 attention (B2 H16 L8192 d64, TFLOP/s on
+active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds).
+
+Timing: inputs are resident in HBM before the timed region; W untimed
+warm-up calls; then K calls, each bracketed by HIP events recorded on the
+stream the kernels run on; the whole region is bracketed by device syncs.
+The CPU baseline times the fp64 oracle on a bounded sample of the headline
+workload, on this host's cores, and scales it to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
+
+KERNEL_SOURCES = {
+    "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
+    "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip",
+}
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "online_softmax_attention_pass_amd", "csrc", name)
+    h = hashlib.sha256(open(p, "rb").read())
+    h.update(open(os.path.join(ROOT, "online_softmax_attention_pass_amd", "csrc", "rf_internal.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the kernel source as it is now; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != source_sha(KERNEL_SOURCES[workload]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Per-call HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, steps):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [a.elapsed_time(b) for a, b in ev]
+        return per, wall
+
+
+def roofline(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def setup_softmax(rf, torch, W):
+    c = W.CONFIGS[2]
+    x = W.softmax_rows_input(2, c["rows"], c["cols"])
+    xd = torch.from_numpy(x).cuda()
+    yd = torch.empty_like(xd)
+    nbytes = 2 * x.size * 4
+    return dict(fn=lambda: rf.rf_softmax_rows(xd, out=yd), work=nbytes, unit="GB/s", bound="hbm",
+                kernel_fn=None, keep=(xd, yd), cfg=c)
+
+
+def setup_prefill(rf, torch, W):
+    c = W.CONFIGS[3]
+    q, k, v = (torch.from_numpy(W.normal_tensor(3, t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
+               .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
+    flops = 4 * c["B"] * c["H"] * c["Lq"] * c["Lk"] * c["d"] / 2   # causal: half of the dense score matrix
+    return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], causal=True, out=o, lse=lse),
+                work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, o, lse), cfg=c)
+
+
+def setup_sparse(rf, torch, W):
+    c = W.CONFIGS[5]
+    q, k, v = (torch.from_numpy(W.normal_tensor(5, t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
+               .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
+    bm = W.config_block_mask(5)
+    bmd = torch.from_numpy(bm).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
+    flops = 4 * 64 * 64 * c["d"] * int(bm.sum()) * c["B"] * c["H"]   # active 64x64 tiles, counted whole
+    return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], causal=True, block_mask=bmd, out=o,
+                                               lse=lse),
+                work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, bmd, o, lse), cfg=c,
+                extra={"active_tiles_per_head": int(bm.sum()), "tiles_per_head": int(bm.size)})
+
+
+def setup_decode(rf, torch, W):
+    c = W.CONFIGS[4]
+    B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
+
+    def up(t, L):
+        a = W.normal_tensor(4, t, B, H, L, d, "bf16")
+        x = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        del a
+        return x
+    log("decode: generating 32 GiB of K/V on the host")
+    q = up(W.TID_Q, 1)
+    k = up(W.TID_K, Lk)
+    v = up(W.TID_V, Lk)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws_bytes = rf.rf_attention_decode_splitkv_workspace_size(B, H, d, S)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    nbytes = 2 * B * H * Lk * d * 2 + B * H * d * 2 * 2 + B * H * 4
+    # the merge alone, on the same workspace layout, to split the two launches' times
+    n = B * H
+    o_parts = ws[: n * S * d * 4].view(torch.float32).view(n, S, d)
+    lse_off = -(-n * S * d * 4 // 256) * 256
+    lse_parts = ws[lse_off: lse_off + n * S * 4].view(torch.float32).view(n, S)
+    o2 = o.view(n, d)
+    lse2 = lse.view(n)
+    merge = lambda: rf.rf_lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=o2, lse=lse2)
+    return dict(fn=lambda: rf.rf_attention_decode_splitkv(q, k, v, scale=c["scale"], num_splits=S, workspace=ws,
+                                                          out=o, lse=lse),
+                work=nbytes, unit="GB/s", bound="hbm", keep=(q, k, v, o, lse, ws), cfg=c, subtract=merge,
+                extra={"workspace_bytes_round_trip": int(2 * n * S * (d + 1) * 4)})
+
+
+def setup_attn_f32(rf, torch, W):
+    c = W.CONFIGS[1]
+    q, k, v = (torch.from_numpy(W.normal_tensor(1, t, 1, 1, 128, 64, "f32")).cuda()
+               for t in (W.TID_Q, W.TID_K, W.TID_V))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
+    flops = 4 * 128 * 128 * 64
+    return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], out=o, lse=lse), work=flops,
+                unit="TFLOP/s", bound="alu", keep=(q, k, v, o, lse), cfg=c)
+
+
+SETUPS = {"softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
+          "attn_f32": setup_attn_f32}
+NAMES = {"softmax": 2, "prefill": 3, "decode": 4, "sparse": 5, "attn_f32": 1}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the headline workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_softmax(W, budget_s=12.0):
+    import oracle
+    c = W.CONFIGS[2]
+    rows = 0
+    spent = 0.0
+    chunk = 64
+    while spent < budget_s and rows < c["rows"]:
+        x = W.softmax_rows_input(2, chunk, c["cols"], row_ids=range(rows, rows + chunk))
+        t0 = time.perf_counter()
+        oracle.softmax_rows(x)
+        spent += time.perf_counter() - t0
+        rows += chunk
+    gbs = 2 * rows * c["cols"] * 4 / spent / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {c['rows']} rows x {c['cols']} cols (fp64 NumPy three-pass softmax, "
+                      f"{spent:.1f} s, single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (no sharding, no collectives). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import online_softmax_attention_pass_amd as rf
+    import workloads as W
+    rf.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    wanted = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    results = {}
+    timer = Timer(torch)
+    for name in wanted:
+        log(f"{name}: setup")
+        s = SETUPS[name](rf, torch, W)
+        for _ in range(args.warmup):
+            s["fn"]()
+        torch.cuda.synchronize()
+        log(f"{name}: timing {args.steps} calls")
+        per, wall = timer.run(s["fn"], args.steps)
+        call_ms = float(np.mean(per))
+        kern_ms = call_ms
+        merge_ms = None
+        if "subtract" in s:
+            for _ in range(args.warmup):
+                s["subtract"]()
+            mper, _ = timer.run(s["subtract"], args.steps)
+            merge_ms = float(np.mean(mper))
+            kern_ms = call_ms - merge_ms
+        thr = s["work"] / (call_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
+        kthr = s["work"] / (kern_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
+        peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS, "alu": FP32_VALU_PEAK_TFLOPS}[s["bound"]]
+        r = {"workload": s["cfg"]["name"], "value": round(thr, 3), "unit": s["unit"],
+             "ms_per_call": round(call_ms, 5), "ms_p10": round(float(np.percentile(per, 10)), 5),
+             "ms_p90": round(float(np.percentile(per, 90)), 5), "wall_s": round(wall, 4),
+             "roofline": roofline(s["bound"], kthr, peak, s["unit"], measured_traffic(name))}
+        if merge_ms is not None:
+            r["merge_ms"] = round(merge_ms, 5)
+            r["partial_kernel_ms"] = round(kern_ms, 5)
+        r.update(s.get("extra", {}))
+        results[name] = r
+        log(f"{name}: {r['value']} {r['unit']} ({call_ms:.4f} ms/call, frac {r['roofline']['frac']})")
+        del s
+        torch.cuda.empty_cache()
+
+    head = "softmax" if "softmax" in results else wanted[0]
+    h = results[head]
+    hc = W.CONFIGS[NAMES[head]]
+    out = {
+        "metric": "fused attention TFLOP/s (% bf16 MFMA peak); softmax/decode GB/s (% HBM peak)",
+        "value": h["value"], "unit": h["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": h["ms_per_call"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if hc["dtype"] == "f32" else "bf16", "data": "synthetic",
+        "config": {"workload": hc["name"], **{k: v for k, v in hc.items() if k in
+                                              ("rows", "cols", "B", "H", "Lq", "Lk", "d", "num_splits")}},
+        "roofline": h["roofline"],
+        "workloads": results,
+    }
+    if not args.no_cpu_baseline and head == "softmax":
+        log("cpu baseline: fp64 oracle on a sample of the softmax workload")
+        out["cpu_baseline"] = cpu_baseline_softmax(W)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * rf.h — C ABI of the fused online-softmax attention library for AMD MI355X (gfx950).
+ *
+ * What is computed is the cascaded reduction behind safe softmax — a row max,
+ * then a sum of exponentials that depends on that max, then a normalisation —
+ * optionally followed by the P·V contraction of attention, run as one pass in
+ * incremental form: a running max m and running sum l are rescaled by
+ * exp(m_old - m_new) as each tile of the reduction axis arrives, so on-chip
+ * state stays constant in sequence length.
+ *
+ * Sources (web summaries of the papers):
+ *   - RedFuser page, "Résumé technique": 1. Problématique (cascaded reductions,
+ *     safe softmax followed by a GEMM in attention), 2. Méthodologie (the
+ *     definition d_i = ⊕ F_i(X[l], D_i), fusion into one reduction tree, the
+ *     incremental form with O(1) on-chip state), 3. Contributions clés
+ *     (single-segment and multi-segment strategies; FlashDecoding as a
+ *     special case of the latter).
+ *   - FLASHLIGHT page, Metodologia item 3 (online softmax via e^{x-y} = e^x/e^y).
+ *   - STOF page, Résumé technique (block masks; skip masked tiles rather than
+ *     compute and reset them; full and partial outer tiles).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer into caller-owned memory. The
+ *     library never allocates or frees device memory and never keeps a
+ *     pointer after a call returns.
+ *   - All tensors are dense, contiguous and row-major.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream. Work is enqueued asynchronously and the call returns once it is
+ *     enqueued; the caller synchronises.
+ *   - Every argument is validated before any HIP API call, so a validation
+ *     error is returned synchronously, enqueues nothing and leaves the
+ *     library usable. A HIP launch failure returns RF_ERR_HIP. The detail of
+ *     the last failing call on the calling thread is in rf_last_error_message().
+ *   - Outputs are fully overwritten, never accumulated into. Inputs must not
+ *     alias outputs.
+ *   - Floating-point arithmetic is fp32 (accumulation, running max and sum);
+ *     bf16 inputs are widened exactly, bf16 outputs are rounded to nearest
+ *     even. LSE values are natural logarithms.
+ *   - No C++ exception crosses this boundary. There is no global mutable
+ *     state besides the thread-local error text, so calls on different
+ *     streams may run concurrently.
+ */
+#ifndef RF_H_
+#define RF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RF_F32 = 0, RF_BF16 = 1 } rf_dtype;
+
+typedef enum {
+  RF_OK = 0,
+  RF_ERR_INVALID_ARG = 1,  /* NULL pointer, negative or overflowing size, bad enum */
+  RF_ERR_UNSUPPORTED = 2,  /* a valid request this build has no kernel for */
+  RF_ERR_WORKSPACE = 3,    /* caller workspace missing or smaller than required */
+  RF_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} rf_status;
+
+/* Tile edge, in tokens, of the attention block mask (both axes). */
+#define RF_MASK_TILE 64
+
+/*
+ * Row-wise safe softmax: y[r, :] = exp(x[r, :] - max_r) / sum_j exp(x[r, j] - max_r).
+ * Source: RedFuser page, 1. Problématique / 2. Méthodologie (max → exp-sum →
+ * normalise as one fused reduction tree, the input read once).
+ *   x, y   : [rows, cols] of `dtype` (RF_F32 or RF_BF16), device pointers.
+ *   rows   : >= 0 (0 enqueues nothing); cols >= 1.
+ * Each element is read once and written once when the row fits on chip
+ * (cols <= 65536); longer rows take a second
+ * read. A row whose entries are all -inf yields NaN.
+ * Errors: RF_ERR_INVALID_ARG (NULL pointer with rows > 0, rows < 0, cols < 1,
+ * rows*cols overflowing int64, unknown dtype).
+ */
+int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype, void* stream);
+
+/*
+ * Attention forward with the online softmax, single-segment strategy (one
+ * workgroup sweeps every visible key tile of its query tile).
+ * Source: RedFuser page, 1. Problématique (safe softmax then GEMM) and
+ * 3. Contributions clés (single-segment strategy); FLASHLIGHT page,
+ * Metodologia 2–4 (max() fused into QK^T, softmax(QK^T)V fused); STOF page,
+ * Méthodologie 1 (block mask, full / partial outer tiles, masked tiles skipped).
+ *   q          : [B, H, Lq, d] of `dtype`.
+ *   k, v       : [B, H, Lk, d] of `dtype`.
+ *   o          : [B, H, Lq, d] of `dtype`, written.
+ *   lse        : [B, H, Lq] fp32, written; may be NULL (then not written).
+ *   scale      : scores are s_ij = scale * (q_i . k_j).
+ *   causal     : nonzero masks key j for query i unless j <= i + (Lk - Lq)
+ *                (bottom-right aligned; identical to the usual mask when Lq == Lk).
+ *   block_mask : NULL (dense), or a device uint8 array [ceil(Lq/64), ceil(Lk/64)];
+ *                tile (I, J) is visible iff block_mask[I * ceil(Lk/64) + J] != 0.
+ *                One mask is shared by all (b, h). Masked tiles are skipped.
+ * Visible(i, j) = causal rule AND block rule AND j < Lk. A query row with no
+ * visible key gets O = 0 and LSE = -inf.
+ * Supported: RF_BF16 with d in {64, 128}; RF_F32 with 1 <= d <= 128.
+ * B, H, Lq, Lk >= 0 (any of B, H, Lq zero enqueues nothing).
+ * Errors: RF_ERR_INVALID_ARG (NULL pointers when work exists, negative sizes,
+ * non-finite scale, unknown dtype), RF_ERR_UNSUPPORTED (other d), RF_ERR_HIP.
+ */
+int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                     const uint8_t* block_mask, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace that rf_attention_decode_splitkv needs:
+ * B*H*num_splits*(d + 1) fp32 values (normalised partial outputs and their
+ * LSE), rounded up to 256 bytes. Returns 0 for invalid arguments.
+ */
+size_t rf_attention_decode_splitkv_workspace_size(int B, int H, int d, int num_splits);
+
+/*
+ * Split-KV decode: one query token per (b, h) against Lk cached keys, with the
+ * multi-segment strategy: the Lk keys are cut into num_splits contiguous
+ * chunks of ceil(Lk / num_splits) keys (trailing chunks may be short or
+ * empty); each chunk yields a normalised partial (O_s, lse_s) and the
+ * partials are merged by log-sum-exp as rf_lse_merge does.
+ * Source: RedFuser page, 3. Contributions clés (multi-segment strategy,
+ * FlashDecoding as its special case); STOF page, Méthodologie 1 (row-wise kernel).
+ *   q          : [B, H, 1, d] of `dtype`;  k, v : [B, H, Lk, d] of `dtype`.
+ *   o          : [B, H, 1, d] of `dtype`, written.
+ *   lse        : [B, H] fp32, written; may be NULL.
+ *   num_splits : 1 .. 1024.
+ *   workspace  : device buffer of at least
+ *                rf_attention_decode_splitkv_workspace_size(B, H, d, num_splits)
+ *                bytes, 256-byte aligned; its contents on entry are ignored.
+ *                It must stay untouched until the enqueued work completes.
+ * No causal or block mask applies: the query sees every cached key. Lk == 0
+ * gives O = 0, LSE = -inf.
+ * Supported: RF_BF16 with d in {64, 128}.
+ * Errors: RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_WORKSPACE (NULL,
+ * misaligned or too small workspace), RF_ERR_HIP.
+ */
+int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Lk, int d, float scale, int num_splits,
+                                void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * Log-sum-exp merge of normalised partial results (the merge step of the
+ * multi-segment strategy; order-free because the (O, lse) pairs form a
+ * commutative monoid with identity (anything, -inf)).
+ * Source: RedFuser page, 2. Méthodologie (fusion conditions: commutative
+ * monoid, distributivity) and 3. Contributions clés (merge of partial results).
+ * Per row r: M = max_s lse[r, s]; w_s = exp(lse[r, s] - M); W = sum_s w_s;
+ *            o[r, :] = sum_s w_s * o_parts[r, s, :] / W;  lse_out[r] = M + ln W.
+ * A part with lse = -inf has weight exactly zero and its o_parts row is not
+ * read. If every part is -inf: o[r, :] = 0 and lse_out[r] = -inf.
+ *   o_parts   : [n_rows, num_splits, d] fp32;  lse_parts : [n_rows, num_splits] fp32.
+ *   o         : [n_rows, d] of out_dtype (RF_F32 or RF_BF16), written.
+ *   lse       : [n_rows] fp32, written; may be NULL.
+ *   n_rows >= 0; 1 <= num_splits <= 1024; d >= 1.
+ * Errors: RF_ERR_INVALID_ARG, RF_ERR_HIP.
+ */
+int rf_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                 int64_t n_rows, int num_splits, int d, int out_dtype, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* rf_status_string(int status);
+
+/* Detail of the last failing call on this thread ("" if none). Valid until
+ * the next rf_* call on the same thread. */
+const char* rf_last_error_message(void);
+
+/* ABI version of this header: bumped when a signature or semantic changes. */
+#define RF_ABI_VERSION 1
+int rf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RF_H_ */

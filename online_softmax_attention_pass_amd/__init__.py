@@ -1,0 +1,219 @@
+"""Python binding of librf, the MI355X online-softmax attention library.
+
+Argument marshalling only: each function checks tensor shapes, dtypes and
+devices, then passes device pointers, sizes and the current HIP stream to the
+C entry point of the same name declared in ``include/rf.h``. Every step of
+the computation runs in the HIP kernels; there is no fallback of any kind, and
+a missing ``librf.so`` is an error.
+
+Build the library with ``python -m online_softmax_attention_pass_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "RF_F32", "RF_BF16", "RFError", "load", "library_path",
+    "rf_softmax_rows", "rf_attention_fwd", "rf_attention_decode_splitkv",
+    "rf_attention_decode_splitkv_workspace_size", "rf_lse_merge", "rf_abi_version",
+]
+
+RF_F32, RF_BF16 = 0, 1
+RF_OK, RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_WORKSPACE, RF_ERR_HIP = 0, 1, 2, 3, 4
+MASK_TILE = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("RF_LIBRARY", os.path.join(_HERE, "librf.so"))
+
+
+class RFError(RuntimeError):
+    def __init__(self, status: int, fn: str, message: str):
+        self.status = status
+        super().__init__(f"{fn} failed with {status}: {message}")
+
+
+def load():
+    """Load librf.so and declare its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"librf.so not found at {path}; build it with "
+                           f"`python -m online_softmax_attention_pass_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "rf_softmax_rows": ([P, P, I64, I64, I, P], I),
+        "rf_attention_fwd": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P], I),
+        "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
+        "rf_attention_decode_splitkv": ([P, P, P, P, P, I, I, I, I, F, I, P, SZ, I, P], I),
+        "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
+        "rf_status_string": ([I], ctypes.c_char_p),
+        "rf_last_error_message": ([], ctypes.c_char_p),
+        "rf_abi_version": ([], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int, fn: str):
+    if status != RF_OK:
+        lib = load()
+        raise RFError(status, fn, lib.rf_last_error_message().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RF_F32
+    if t.dtype == torch.bfloat16:
+        return RF_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev):
+    return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0) if t is not None \
+        else ctypes.c_void_p(0)
+
+
+def rf_abi_version() -> int:
+    return load().rf_abi_version()
+
+
+def rf_softmax_rows(x, out=None):
+    """Safe softmax over the last dimension of a contiguous fp32 / bf16 tensor."""
+    torch = _torch()
+    lib = load()
+    if x.dim() < 1 or x.shape[-1] < 1:
+        raise ValueError("x needs a non-empty last dimension")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    dev = _dev(x, y)
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    _check(lib.rf_softmax_rows(_ptr(x), _ptr(y), rows, cols, _dtype_code(x), _stream(dev)), "rf_softmax_rows")
+    return y
+
+
+def rf_attention_fwd(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, want_lse=True):
+    """Attention forward. q [B,H,Lq,d]; k, v [B,H,Lk,d]; block_mask uint8 [ceil(Lq/64), ceil(Lk/64)] or None.
+
+    Returns (o, lse) with o like q and lse fp32 [B,H,Lq] (None if want_lse is False).
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if block_mask is not None:
+        want = (math.ceil(Lq / MASK_TILE), math.ceil(Lk / MASK_TILE))
+        if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != want:
+            raise ValueError(f"block_mask must be uint8 {want}")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be fp32 [B, H, Lq]")
+    dev = _dev(q, k, v, o, lse, block_mask)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.rf_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
+                              1 if causal else 0, _ptr(block_mask), _dtype_code(q), _stream(dev))
+    _check(st, "rf_attention_fwd")
+    return o, lse
+
+
+def rf_attention_decode_splitkv_workspace_size(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(load().rf_attention_decode_splitkv_workspace_size(B, H, d, num_splits))
+
+
+def rf_attention_decode_splitkv(q, k, v, scale=None, num_splits=16, workspace=None, out=None, lse=None,
+                                want_lse=True):
+    """Split-KV decode. q [B,H,1,d]; k, v [B,H,Lk,d] (bf16). Returns (o [B,H,1,d], lse [B,H])."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    B, H, _, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError("k, v must be [B, H, Lk, d] matching q")
+    ws_bytes = rf_attention_decode_splitkv_workspace_size(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    dev = _dev(q, k, v, o, lse, workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = lib.rf_attention_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lk, d,
+                                         float(scale), num_splits, _ptr(workspace), nbytes, _dtype_code(q),
+                                         _stream(dev))
+    _check(st, "rf_attention_decode_splitkv")
+    return o, lse
+
+
+def rf_lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse=None, want_lse=True):
+    """Merge normalised partials: o_parts fp32 [n, S, d], lse_parts fp32 [n, S] -> (o [n, d], lse [n])."""
+    torch = _torch()
+    lib = load()
+    n, S, d = o_parts.shape
+    if lse_parts.shape != (n, S):
+        raise ValueError("lse_parts must be [n, S]")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    o = torch.empty((n, d), dtype=out_dtype, device=o_parts.device) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((n,), dtype=torch.float32, device=o_parts.device)
+    dev = _dev(o_parts, lse_parts, o, lse)
+    st = lib.rf_lse_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse), n, S, d, _dtype_code(o),
+                          _stream(dev))
+    _check(st, "rf_lse_merge")
+    return o, lse

@@ -1,0 +1,238 @@
+// C-ABI entry points of librf: argument validation, dispatch, error reporting.
+//
+// Every check runs before the first HIP API call of an entry point, so a
+// rejected call is synchronous, enqueues nothing and needs no GPU. Kernels
+// are launched asynchronously on the caller's stream. No C++ exception
+// crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <exception>
+#include <string>
+
+#include "rf.h"
+#include "rf_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return RF_OK;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(RF_ERR_HIP, "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+// a * b * c * ... without int64 overflow; false when the product would overflow.
+bool mul_ok(int64_t& acc, int64_t x) {
+  if (x < 0) return false;
+  if (x != 0 && acc > INT64_MAX / x) return false;
+  acc *= x;
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct DecodeWs {
+  size_t o_bytes, lse_off, total;
+};
+
+bool decode_ws_layout(int B, int H, int d, int S, DecodeWs& w) {
+  if (B < 0 || H < 0 || d < 1 || S < 1 || S > 1024) return false;
+  int64_t n = 1;
+  if (!mul_ok(n, B) || !mul_ok(n, H) || !mul_ok(n, S)) return false;
+  int64_t nod = n;
+  if (!mul_ok(nod, d) || !mul_ok(nod, 4)) return false;
+  if (n > INT64_MAX / 8) return false;
+  w.o_bytes = size_t(nod);
+  w.lse_off = round_up(w.o_bytes, 256);
+  w.total = w.lse_off + round_up(size_t(n) * 4, 256);
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rf_status_string(int s) {
+  switch (s) {
+    case RF_OK: return "RF_OK";
+    case RF_ERR_INVALID_ARG: return "RF_ERR_INVALID_ARG";
+    case RF_ERR_UNSUPPORTED: return "RF_ERR_UNSUPPORTED";
+    case RF_ERR_WORKSPACE: return "RF_ERR_WORKSPACE";
+    case RF_ERR_HIP: return "RF_ERR_HIP";
+    default: return "RF_UNKNOWN_STATUS";
+  }
+}
+
+const char* rf_last_error_message(void) { return g_last_error.c_str(); }
+
+int rf_abi_version(void) { return RF_ABI_VERSION; }
+
+int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype, void* stream) {
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: unknown dtype %d", dtype);
+    if (rows < 0) return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: rows = %lld < 0", (long long)rows);
+    if (cols < 1) return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: cols = %lld < 1", (long long)cols);
+    int64_t n = rows;
+    if (!mul_ok(n, cols) || !mul_ok(n, dtype == RF_F32 ? 4 : 2))
+      return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: rows * cols overflows");
+    if (rows == 0) return ok();
+    if (x == nullptr || y == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: NULL x or y");
+    const size_t es = dtype == RF_F32 ? 4 : 2;
+    if (!aligned(x, es) || !aligned(y, es))
+      return fail(RF_ERR_INVALID_ARG, "rf_softmax_rows: x and y must be aligned to their element size");
+    return hip_status(rf::launch_softmax_rows(x, y, rows, cols, dtype, static_cast<hipStream_t>(stream)),
+                      "rf_softmax_rows");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "rf_softmax_rows: %s", e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "rf_softmax_rows: unknown exception");
+  }
+}
+
+int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                     int Lk, int d, float scale, int causal, const uint8_t* block_mask, int dtype, void* stream) {
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16)
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: unknown dtype %d", dtype);
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0)
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: negative size (B=%d H=%d Lq=%d Lk=%d)", B, H, Lq, Lk);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: d = %d < 1", d);
+    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: scale is not finite");
+    if (dtype == RF_BF16 && d != 64 && d != 128)
+      return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: bf16 supports d in {64, 128}, got %d", d);
+    if (dtype == RF_F32 && d > 128)
+      return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: fp32 supports d <= 128, got %d", d);
+    const int es = dtype == RF_F32 ? 4 : 2;
+    int64_t nq = 1, nk = 1;
+    if (!mul_ok(nq, B) || !mul_ok(nq, H) || !mul_ok(nq, Lq) || !mul_ok(nq, d) || !mul_ok(nq, es) ||
+        !mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, es))
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: tensor size overflows int64");
+    if (int64_t(B) * H * Lq == 0) return ok();
+    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL q or o");
+    if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL k or v");
+    if (dtype == RF_BF16) {
+      if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
+        return fail(RF_ERR_UNSUPPORTED,
+                    "rf_attention_fwd: bf16 path needs 16-byte aligned q, k, v and 8-byte aligned o");
+    } else if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) {
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: fp32 tensors must be 4-byte aligned");
+    }
+    if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: lse misaligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e =
+        dtype == RF_BF16
+            ? rf::launch_attention_bf16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, block_mask, s)
+            : rf::launch_attention_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                       static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, Lq, Lk,
+                                       d, scale, causal != 0, block_mask, s);
+    return hip_status(e, "rf_attention_fwd");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "rf_attention_fwd: %s", e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "rf_attention_fwd: unknown exception");
+  }
+}
+
+size_t rf_attention_decode_splitkv_workspace_size(int B, int H, int d, int num_splits) {
+  DecodeWs w;
+  if (!decode_ws_layout(B, H, d, num_splits, w)) return 0;
+  return w.total;
+}
+
+int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                int Lk, int d, float scale, int num_splits, void* workspace,
+                                size_t workspace_bytes, int dtype, void* stream) {
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16)
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: unknown dtype %d", dtype);
+    if (B < 0 || H < 0 || Lk < 0)
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: negative size (B=%d H=%d Lk=%d)", B, H, Lk);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: d = %d < 1", d);
+    if (num_splits < 1 || num_splits > 1024)
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: num_splits = %d outside 1..1024", num_splits);
+    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: scale is not finite");
+    if (dtype != RF_BF16) return fail(RF_ERR_UNSUPPORTED, "rf_attention_decode_splitkv: only bf16 is supported");
+    if (d != 64 && d != 128)
+      return fail(RF_ERR_UNSUPPORTED, "rf_attention_decode_splitkv: d must be 64 or 128, got %d", d);
+    int64_t nk = 1;
+    if (!mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, 2))
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: tensor size overflows int64");
+    DecodeWs w;
+    if (!decode_ws_layout(B, H, d, num_splits, w))
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: workspace size overflows");
+    if (int64_t(B) * H == 0) return ok();
+    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: NULL q or o");
+    if (Lk > 0 && (k == nullptr || v == nullptr))
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: NULL k or v");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
+      return fail(RF_ERR_UNSUPPORTED,
+                  "rf_attention_decode_splitkv: needs 16-byte aligned q, k, v and 8-byte aligned o");
+    if (lse != nullptr && !aligned(lse, 4))
+      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: lse misaligned");
+    if (workspace == nullptr || workspace_bytes < w.total || !aligned(workspace, 256))
+      return fail(RF_ERR_WORKSPACE,
+                  "rf_attention_decode_splitkv: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
+                  w.total, workspace_bytes, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* o_parts = static_cast<float*>(workspace);
+    float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lse_off);
+    hipError_t e = rf::launch_decode_partials(q, k, v, o_parts, lse_parts, B, H, Lk, d, scale, num_splits, s);
+    if (e != hipSuccess) return hip_status(e, "rf_attention_decode_splitkv (partials)");
+    e = rf::launch_lse_merge(o_parts, lse_parts, o, lse, int64_t(B) * H, num_splits, d, RF_BF16, s);
+    return hip_status(e, "rf_attention_decode_splitkv (merge)");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "rf_attention_decode_splitkv: %s", e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "rf_attention_decode_splitkv: unknown exception");
+  }
+}
+
+int rf_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int64_t n_rows, int num_splits,
+                 int d, int out_dtype, void* stream) {
+  try {
+    if (out_dtype != RF_F32 && out_dtype != RF_BF16)
+      return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: unknown out_dtype %d", out_dtype);
+    if (n_rows < 0) return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: n_rows < 0");
+    if (num_splits < 1 || num_splits > 1024)
+      return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: num_splits = %d outside 1..1024", num_splits);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: d = %d < 1", d);
+    int64_t n = n_rows;
+    if (!mul_ok(n, num_splits) || !mul_ok(n, d) || !mul_ok(n, 4))
+      return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: size overflows int64");
+    if (n_rows == 0) return ok();
+    if (o_parts == nullptr || lse_parts == nullptr || o == nullptr)
+      return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: NULL o_parts, lse_parts or o");
+    if (!aligned(o_parts, 4) || !aligned(lse_parts, 4) || !aligned(o, out_dtype == RF_F32 ? 4 : 2) ||
+        (lse != nullptr && !aligned(lse, 4)))
+      return fail(RF_ERR_INVALID_ARG, "rf_lse_merge: misaligned pointer");
+    return hip_status(rf::launch_lse_merge(o_parts, lse_parts, o, lse, n_rows, num_splits, d, out_dtype,
+                                           static_cast<hipStream_t>(stream)),
+                      "rf_lse_merge");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "rf_lse_merge: %s", e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "rf_lse_merge: unknown exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Row-wise safe softmax as one fused reduction tree over a single read of the row.
+//
+// The cascade max -> sum of exp(x - max) -> normalise (RedFuser page, Résumé
+// technique, 1. Problématique; d_i = ⊕ F_i(X[l], D_i) in 2. Méthodologie) is
+// fused with the rescale identity e^{x-y} = e^x / e^y (FLASHLIGHT page,
+// Metodologia 3): each lane reduces its own elements to a pair (m_t, l_t),
+// and the pairs meet in ONE tree under
+//   (m_a, l_a) (+) (m_b, l_b) = (M, l_a e^{m_a - M} + l_b e^{m_b - M}).
+// The row stays in registers between the reduction and the normalisation, so
+// every element is read from HBM once and written once (single-segment
+// strategy: one workgroup owns one row, no inter-workgroup synchronisation).
+// Rows longer than a workgroup's register capacity take a streaming variant:
+// one online (m, l) read, then a normalising read + write.
+#include <stdint.h>
+
+#include "rf_internal.h"
+
+namespace rf {
+namespace {
+
+// Element access: fp32 or bf16 (raw bits), as 16-byte vectors of EPV elements
+// or single elements (EPV = 1) when the row is not 16-byte aligned.
+template <typename T, int EPV> struct Io;
+
+template <> struct Io<float, 4> {
+  __device__ static void load(const float* p, float (&o)[4]) {
+    const float4 v = nt_load(reinterpret_cast<const float4*>(p));
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void store(float* p, const float (&o)[4]) {
+    float4 v = make_float4(o[0], o[1], o[2], o[3]);
+    nt_store(v, reinterpret_cast<float4*>(p));
+  }
+};
+template <> struct Io<float, 1> {
+  __device__ static void load(const float* p, float (&o)[1]) { o[0] = *p; }
+  __device__ static void store(float* p, const float (&o)[1]) { *p = o[0]; }
+};
+template <> struct Io<uint16_t, 8> {
+  __device__ static void load(const uint16_t* p, float (&o)[8]) {
+    const uint4 v = nt_load(reinterpret_cast<const uint4*>(p));
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+  }
+  __device__ static void store(uint16_t* p, const float (&o)[8]) {
+    uint4 v;
+    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+    nt_store(v, reinterpret_cast<uint4*>(p));
+  }
+};
+template <> struct Io<uint16_t, 1> {
+  __device__ static void load(const uint16_t* p, float (&o)[1]) { o[0] = bf16_to_f32(*p); }
+  __device__ static void store(uint16_t* p, const float (&o)[1]) { *p = uint16_t(f32_to_bf16_bits(o[0])); }
+};
+
+// Workgroup-wide (+)-reduction of (m, l): wavefront butterfly, then LDS across waves.
+template <int BLOCK>
+__device__ __forceinline__ void block_combine(float& m, float& l, float* sm, float* sl) {
+  constexpr int NW = BLOCK / 64;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = shfl_xor(m, off);
+    const float l2 = shfl_xor(l, off);
+    ml_combine_nat(m, l, m2, l2);
+  }
+  if constexpr (NW > 1) {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sm[w] = m; sl[w] = l; }
+    __syncthreads();
+    m = sm[0];
+    l = sl[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) ml_combine_nat(m, l, sm[i], sl[i]);
+  }
+}
+
+// Register-resident row: thread t owns vectors t, t + BLOCK, ..., t + (NV-1) BLOCK.
+template <typename T, int EPV, int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void softmax_rows_reg(const T* __restrict__ x, T* __restrict__ y,
+                                                          int64_t rows, int64_t cols) {
+  __shared__ float sm[BLOCK / 64], sl[BLOCK / 64];
+  const int64_t nvec = cols / EPV;  // the host guarantees cols % EPV == 0
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const T* xr = x + r * cols;
+    T* yr = y + r * cols;
+    float v[NV][EPV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t vi = threadIdx.x + int64_t(k) * BLOCK;
+      if (vi < nvec) {
+        Io<T, EPV>::load(xr + vi * EPV, v[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) v[k][e] = kNegInf;
+      }
+    }
+    // Lane-local pair: m_t = max of its elements, l_t = sum_e e^{x_e - m_t}.
+    float m = kNegInf;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) m = fmaxf(m, v[k][e]);
+    const float mu = (m == kNegInf) ? 0.f : m;
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        v[k][e] = fast_exp2((v[k][e] - mu) * kLog2e);
+        l += v[k][e];
+      }
+    float M = m, L = l;
+    block_combine<BLOCK>(M, L, sm, sl);
+    // y = e^{x - m_t} * e^{m_t - M} / L  (an all -inf row gives NaN, as the definition does)
+    const float c = fast_exp2((m - M) * kLog2e) / L;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int64_t vi = threadIdx.x + int64_t(k) * BLOCK;
+      if (vi < nvec) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) v[k][e] *= c;
+        Io<T, EPV>::store(yr + vi * EPV, v[k]);
+      }
+    }
+    if (BLOCK > 64 && r + gridDim.x < rows) __syncthreads();  // sm/sl reused by the next row
+  }
+}
+
+// Rows too long for registers: an online (m, l) pass, then a normalising pass.
+template <typename T, int EPV, int BLOCK>
+__global__ __launch_bounds__(BLOCK) void softmax_rows_stream(const T* __restrict__ x, T* __restrict__ y,
+                                                             int64_t rows, int64_t cols) {
+  __shared__ float sm[BLOCK / 64], sl[BLOCK / 64];
+  const int64_t nvec = cols / EPV;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const T* xr = x + r * cols;
+    T* yr = y + r * cols;
+    float m = kNegInf, l = 0.f;  // running pair, m in natural units
+    for (int64_t vi = threadIdx.x; vi < nvec; vi += BLOCK) {
+      float a[EPV];
+      Io<T, EPV>::load(xr + vi * EPV, a);
+      float bm = kNegInf;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) bm = fmaxf(bm, a[e]);
+      const float mn = fmaxf(m, bm);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) s += fast_exp2((a[e] - mu) * kLog2e);
+      l = l * fast_exp2((m - mu) * kLog2e) + s;  // rescale when the running max moves
+      m = mn;
+    }
+    block_combine<BLOCK>(m, l, sm, sl);
+    const float inv = 1.f / l;
+    for (int64_t vi = threadIdx.x; vi < nvec; vi += BLOCK) {
+      float a[EPV];
+      Io<T, EPV>::load(xr + vi * EPV, a);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) a[e] = fast_exp2((a[e] - m) * kLog2e) * inv;
+      Io<T, EPV>::store(yr + vi * EPV, a);
+    }
+    if (r + gridDim.x < rows) __syncthreads();
+  }
+}
+
+// Register-resident variants, smallest first: (lanes per workgroup, floats per lane).
+// At most 64 row elements live in each lane, so even the 1024-lane variant
+// (16 waves, 4 per SIMD) stays within 128 VGPRs without spilling.
+template <typename T, int EPV>
+hipError_t dispatch(const T* x, T* y, int64_t rows, int64_t cols, hipStream_t stream) {
+  const int64_t nvec = cols / EPV;
+  const unsigned grid = unsigned(rows < (1 << 30) ? rows : (1 << 30));
+#define RF_SOFTMAX_REG(BLOCK, FPL)                                                                  \
+  if (nvec <= int64_t(BLOCK) * ((FPL) / EPV)) {                                                    \
+    hipLaunchKernelGGL((softmax_rows_reg<T, EPV, BLOCK, (FPL) / EPV>), dim3(grid), dim3(BLOCK), 0, \
+                       stream, x, y, rows, cols);                                                  \
+    return hipGetLastError();                                                                      \
+  }
+  RF_SOFTMAX_REG(64, 16)
+  RF_SOFTMAX_REG(128, 32)
+  RF_SOFTMAX_REG(256, 32)
+  RF_SOFTMAX_REG(512, 32)
+  RF_SOFTMAX_REG(512, 64)
+  RF_SOFTMAX_REG(1024, 64)
+#undef RF_SOFTMAX_REG
+  hipLaunchKernelGGL((softmax_rows_stream<T, EPV, 1024>), dim3(grid), dim3(1024), 0, stream, x, y,
+                     rows, cols);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype,
+                               hipStream_t stream) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (reinterpret_cast<uintptr_t>(y) % 16 == 0);
+  if (dtype == 0) {
+    const float* xf = static_cast<const float*>(x);
+    float* yf = static_cast<float*>(y);
+    if (aligned && cols % 4 == 0) return dispatch<float, 4>(xf, yf, rows, cols, stream);
+    return dispatch<float, 1>(xf, yf, rows, cols, stream);
+  }
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* yb = static_cast<uint16_t*>(y);
+  if (aligned && cols % 8 == 0) return dispatch<uint16_t, 8>(xb, yb, rows, cols, stream);
+  return dispatch<uint16_t, 1>(xb, yb, rows, cols, stream);
+}
+
+}  // namespace rf

@@ -1,0 +1,188 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+``include/rf.h`` declares, and rejects bad arguments before any HIP call.
+
+Every call here either fails validation or has no work (rows = 0, B = 0, ...),
+so nothing reaches the HIP runtime.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import online_softmax_attention_pass_amd as rf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rf.h")
+
+OK, INVALID, UNSUP, WS = rf.RF_OK, rf.RF_ERR_INVALID_ARG, rf.RF_ERR_UNSUPPORTED, rf.RF_ERR_WORKSPACE
+F32, BF16 = rf.RF_F32, rf.RF_BF16
+P = ctypes.c_void_p
+FAKE = P(0x10000)            # a non-NULL, 256-byte-aligned address that is never dereferenced
+NUL = P(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rf.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rf_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"rf_softmax_rows", "rf_attention_fwd", "rf_attention_decode_splitkv", "rf_lse_merge"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"librf.so does not export {n}"
+
+
+def test_exports_no_cxx_names_for_the_abi(lib):
+    # the entry points are plain C symbols (no mangling)
+    out = os.popen(f"nm -D --defined-only {rf.library_path()}").read()
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_abi_version(lib):
+    assert lib.rf_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.rf_status_string(OK) == b"RF_OK"
+    assert lib.rf_status_string(INVALID) == b"RF_ERR_INVALID_ARG"
+    assert lib.rf_status_string(UNSUP) == b"RF_ERR_UNSUPPORTED"
+    assert lib.rf_status_string(WS) == b"RF_ERR_WORKSPACE"
+    assert lib.rf_status_string(rf.RF_ERR_HIP) == b"RF_ERR_HIP"
+    assert lib.rf_status_string(99) == b"RF_UNKNOWN_STATUS"
+
+
+def _msg(lib):
+    return lib.rf_last_error_message().decode()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NUL, NUL, 4, 8, F32), INVALID),          # NULL with work
+    ((FAKE, FAKE, -1, 8, F32), INVALID),       # rows < 0
+    ((FAKE, FAKE, 4, 0, F32), INVALID),        # cols < 1
+    ((FAKE, FAKE, 4, 8, 7), INVALID),          # dtype
+    ((FAKE, FAKE, 1 << 40, 1 << 40, F32), INVALID),   # overflow
+    ((FAKE, P(0x10001), 4, 8, F32), INVALID),  # misaligned fp32
+    ((NUL, NUL, 0, 8, F32), OK),               # no rows: nothing to do
+    ((NUL, NUL, 0, 8, BF16), OK),
+])
+def test_softmax_validation(lib, args, code):
+    assert lib.rf_softmax_rows(*args, NUL) == code
+    assert (_msg(lib) == "") == (code == OK)
+
+
+ATT = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=3, Lq=100, Lk=90, d=128, scale=0.1, causal=1,
+           mask=NUL, dtype=BF16)
+
+
+def att(lib, **kw):
+    a = dict(ATT, **kw)
+    return lib.rf_attention_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"],
+                                a["d"], a["scale"], a["causal"], a["mask"], a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), INVALID),
+    (dict(B=-1), INVALID), (dict(H=-2), INVALID), (dict(Lq=-1), INVALID), (dict(Lk=-5), INVALID),
+    (dict(d=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(d=96), UNSUP), (dict(d=32), UNSUP), (dict(d=256), UNSUP),
+    (dict(dtype=F32, d=129), UNSUP),
+    (dict(q=NUL), INVALID), (dict(o=NUL), INVALID), (dict(k=NUL), INVALID), (dict(v=NUL), INVALID),
+    (dict(q=P(0x10008)), UNSUP),                       # bf16 path needs 16-byte rows
+    (dict(dtype=F32, d=33, q=P(0x10002)), INVALID),     # fp32 misaligned
+    (dict(B=0), OK), (dict(H=0), OK), (dict(Lq=0), OK),
+    (dict(B=0, q=NUL, k=NUL, v=NUL, o=NUL), OK),
+    (dict(B=1 << 20, H=1 << 20, Lq=1 << 20), INVALID),  # overflow
+])
+def test_attention_validation(lib, kw, code):
+    assert att(lib, **kw) == code
+    if code != OK:
+        assert "rf_attention_fwd" in _msg(lib)
+
+
+def test_library_usable_after_error(lib):
+    assert att(lib, d=96) == UNSUP
+    assert _msg(lib) != ""
+    assert att(lib, B=0) == OK
+    assert _msg(lib) == ""
+
+
+def test_decode_workspace_size(lib):
+    B, H, d, S = 64, 32, 128, 16
+    n = B * H * S
+    want = -(-n * d * 4 // 256) * 256 + -(-n * 4 // 256) * 256
+    assert lib.rf_attention_decode_splitkv_workspace_size(B, H, d, S) == want
+    assert lib.rf_attention_decode_splitkv_workspace_size(1, 1, 64, 3) == 768 + 256
+    assert lib.rf_attention_decode_splitkv_workspace_size(1, 1, 64, 5) == 1280 + 256
+    assert lib.rf_attention_decode_splitkv_workspace_size(-1, 1, 64, 3) == 0
+    assert lib.rf_attention_decode_splitkv_workspace_size(1, 1, 64, 0) == 0
+    assert lib.rf_attention_decode_splitkv_workspace_size(1, 1, 64, 1025) == 0
+
+
+DEC = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=4, H=2, Lk=1000, d=128, scale=0.1, S=16, ws=FAKE,
+           ws_bytes=1 << 30, dtype=BF16)
+
+
+def dec(lib, **kw):
+    a = dict(DEC, **kw)
+    return lib.rf_attention_decode_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lk"],
+                                           a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), INVALID), (dict(B=-1), INVALID), (dict(Lk=-1), INVALID), (dict(d=0), INVALID),
+    (dict(S=0), INVALID), (dict(S=1025), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP),
+    (dict(q=NUL), INVALID), (dict(o=NUL), INVALID), (dict(k=NUL), INVALID),
+    (dict(ws=NUL), WS), (dict(ws_bytes=100), WS), (dict(ws=P(0x10010)), WS),
+    (dict(q=P(0x10008)), UNSUP),
+    (dict(B=0), OK), (dict(H=0, ws=NUL, ws_bytes=0), OK),
+])
+def test_decode_validation(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, FAKE, 10, 4, 128, 5), INVALID),      # out dtype
+    ((FAKE, FAKE, FAKE, FAKE, -1, 4, 128, F32), INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 10, 0, 128, F32), INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 10, 1025, 128, F32), INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 10, 4, 0, F32), INVALID),
+    ((NUL, FAKE, FAKE, FAKE, 10, 4, 128, F32), INVALID),
+    ((FAKE, NUL, FAKE, FAKE, 10, 4, 128, F32), INVALID),
+    ((FAKE, FAKE, NUL, FAKE, 10, 4, 128, F32), INVALID),
+    ((FAKE, FAKE, FAKE, FAKE, 1 << 50, 1000, 1000, F32), INVALID),
+    ((NUL, NUL, NUL, NUL, 0, 4, 128, BF16), OK),
+])
+def test_lse_merge_validation(lib, args, code):
+    assert lib.rf_lse_merge(*args, NUL) == code
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setenv("RF_LIBRARY", str(tmp_path / "missing.so"))
+    mod = importlib.reload(rf)
+    try:
+        with pytest.raises(RuntimeError, match="librf.so not found"):
+            mod.load()
+    finally:
+        monkeypatch.delenv("RF_LIBRARY")
+        importlib.reload(rf)
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "online_softmax_attention_pass_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b|oracle/", text), f

@@ -1,0 +1,119 @@
+"""Parity at the five workload sizes, in the launch configuration the benchmark times.
+
+Inputs are the seeded draws of ``workloads`` at full size. The oracle checks
+sampled outputs it can compute one by one (whole heads or chosen query rows,
+including tile edges), and cheap whole-output properties are checked on the
+device side. Gates: fp32 outputs 1e-5, bf16 outputs 1e-2, LSE 1e-3 (max abs).
+The bf16 output-rounding floor max|bf16(O) - O| is printed alongside.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_close, dev_bf16, dev_f32, host_f64, max_abs_err, note
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def _report(name, err_o, err_l, ref_o=None):
+    floor = "" if ref_o is None else f" bf16 floor {max_abs_err(O.round_to_bf16(ref_o), ref_o):.3e}"
+    print(f"\n[parity] {name}: max|dO| {err_o:.3e} max|dLSE| {err_l:.3e}{floor}", flush=True)
+
+
+def _qkv_full(cfg):
+    c = W.CONFIGS[cfg]
+    return [W.normal_tensor(cfg, tid, c["B"], c["H"], L, c["d"], c["dtype"])
+            for tid, L in ((W.TID_Q, c.get("Lq", 1)), (W.TID_K, c["Lk"]), (W.TID_V, c["Lk"]))]
+
+
+def test_config1_attention_f32(rf_gpu):
+    c = W.CONFIGS[1]
+    q, k, v = _qkv_full(1)
+    note("config 1 full")
+    o, lse = rf_gpu.rf_attention_fwd(dev_f32(q), dev_f32(k), dev_f32(v), scale=c["scale"], causal=False)
+    ref_o, ref_lse = O.attention(q, k, v, c["scale"])
+    e_o = assert_close(host_f64(o), ref_o, 1e-5, "config 1 O")
+    e_l = assert_close(host_f64(lse), ref_lse, 1e-3, "config 1 LSE")
+    _report("config1", e_o, e_l)
+
+
+def test_config2_softmax_rows(rf_gpu):
+    import torch
+    c = W.CONFIGS[2]
+    x = W.softmax_rows_input(2, c["rows"], c["cols"])
+    note("config 2 full")
+    y = rf_gpu.rf_softmax_rows(dev_f32(x))
+    sums = y.double().sum(dim=1)
+    assert float((sums - 1).abs().max()) < 1e-4                  # every row sums to 1
+    assert bool(torch.isfinite(y).all()) and float(y.min()) >= 0
+    rows = sorted({0, 1, 63, 64, 2047, 2048, 4094, 4095, *W.rng(2, 99).choice(4096, 56, replace=False).tolist()})
+    got = host_f64(y[rows])
+    e = assert_close(got, O.softmax_rows(x[rows]), 1e-5, "config 2 y")
+    _report("config2 (64 sampled rows)", e, 0.0)
+
+
+def _sample_rows(L, seed):
+    edge = {0, 1, 2, 31, 32, 63, 64, 65, 127, 128, 129, 255, 256, L // 2 - 1, L // 2, L - 129, L - 128, L - 65,
+            L - 64, L - 2, L - 1}
+    rand = W.rng(seed, 98).choice(L, 24, replace=False).tolist()
+    return sorted(r for r in edge | set(rand) if 0 <= r < L)
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_config_attention_bf16(rf_gpu, cfg):
+    import torch
+    c = W.CONFIGS[cfg]
+    q, k, v = _qkv_full(cfg)
+    bm = W.config_block_mask(cfg)
+    note(f"config {cfg} full")
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=c["scale"], causal=c["causal"],
+                                     block_mask=None if bm is None else torch.from_numpy(bm).cuda())
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    heads = [(0, 0), (c["B"] - 1, c["H"] - 1), (c["B"] // 2, c["H"] // 3), (0, c["H"] - 2)]
+    rows = _sample_rows(c["Lq"], cfg)
+    worst_o = worst_l = 0.0
+    refs = []
+    for b, h in heads:
+        ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(q[b:b + 1, h:h + 1]), O.bf16_bits_to_f64(k[b:b + 1, h:h + 1]),
+                                     O.bf16_bits_to_f64(v[b:b + 1, h:h + 1]), c["scale"], c["causal"], bm,
+                                     q_rows=rows)
+        got_o = host_f64(o[b, h, rows])
+        got_l = host_f64(lse[b, h, rows])
+        worst_o = max(worst_o, max_abs_err(got_o, ref_o[0, 0]))
+        worst_l = max(worst_l, max_abs_err(got_l, ref_lse[0, 0]))
+        refs.append(ref_o[0, 0])
+    _report(f"config{cfg} ({len(heads)} heads x {len(rows)} rows)", worst_o, worst_l, np.concatenate(refs))
+    assert worst_o <= 1e-2 and worst_l <= 1e-3
+
+
+def test_config4_decode(rf_gpu):
+    import torch
+    c = W.CONFIGS[4]
+    B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
+    q = W.normal_tensor(4, W.TID_Q, B, H, 1, d, "bf16")
+    note("config 4: generating K/V (32 GiB)")
+    k = W.normal_tensor(4, W.TID_K, B, H, Lk, d, "bf16")
+    kd = dev_bf16(k)
+    del k
+    v = W.normal_tensor(4, W.TID_V, B, H, Lk, d, "bf16")
+    vd = dev_bf16(v)
+    del v
+    note("config 4 full")
+    o, lse = rf_gpu.rf_attention_decode_splitkv(dev_bf16(q), kd, vd, scale=c["scale"], num_splits=S)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    heads = [(0, 0), (B - 1, H - 1), (17, 5), (40, 30), (63, 0), (5, 16)]
+    worst_o = worst_l = 0.0
+    refs = []
+    for b, h in heads:
+        kh = W.normal_head(4, W.TID_K, b, h, Lk, d, "bf16")[None, None]
+        vh = W.normal_head(4, W.TID_V, b, h, Lk, d, "bf16")[None, None]
+        ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(q[b:b + 1, h:h + 1]), O.bf16_bits_to_f64(kh),
+                                     O.bf16_bits_to_f64(vh), c["scale"])
+        worst_o = max(worst_o, max_abs_err(host_f64(o[b, h]), ref_o[0, 0]))
+        worst_l = max(worst_l, max_abs_err(host_f64(lse[b, h:h + 1]), ref_lse[0, 0]))
+        refs.append(ref_o[0, 0])
+    _report(f"config4 ({len(heads)} heads)", worst_o, worst_l, np.concatenate(refs))
+    assert worst_o <= 1e-2 and worst_l <= 1e-3

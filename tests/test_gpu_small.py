@@ -1,0 +1,280 @@
+"""GPU parity against the fp64 oracle on small and edge-case shapes.
+
+Sizes span several tiles and ragged tails; every call goes through the C ABI
+(via the binding). Tolerances: fp32 outputs 1e-5 max abs, bf16 outputs 1e-2
+max abs, LSE 1e-3 max abs (tighter where the arithmetic allows it).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_close, dev_bf16, dev_f32, host_f64, note
+
+pytestmark = pytest.mark.gpu
+
+
+def _normal(seed, tid, shape, dtype):
+    z = W.rng(seed, tid).standard_normal(shape, dtype=np.float32)
+    return W.f32_to_bf16_bits(z) if dtype == "bf16" else z
+
+
+def _widen(a, dtype):
+    return O.bf16_bits_to_f64(a) if dtype == "bf16" else a.astype(np.float64)
+
+
+def _dev(a, dtype):
+    return dev_bf16(a) if dtype == "bf16" else dev_f32(a)
+
+
+# ---------------------------------------------------------------------------
+# softmax rows
+# ---------------------------------------------------------------------------
+
+SOFTMAX_SHAPES = [(1, 1), (3, 7), (5, 100), (4, 1024), (3, 4095), (2, 4096), (2, 32768), (2, 65536),
+                  (2, 65540), (2, 70001), (300, 33)]
+
+
+@pytest.mark.parametrize("rows,cols", SOFTMAX_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_rows_small(rf_gpu, rows, cols, dtype):
+    r = W.rng(100, rows, cols)
+    x = (r.standard_normal((rows, cols)) * 2 + r.uniform(-50, 50, (rows, 1))).astype(np.float32)
+    xs = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    note(f"softmax {rows}x{cols} {dtype}")
+    y = rf_gpu.rf_softmax_rows(_dev(xs, dtype))
+    ref = O.softmax_rows(_widen(xs, dtype))
+    if dtype == "f32":
+        assert_close(host_f64(y), ref, 1e-5, "softmax f32")
+    else:
+        got = host_f64(y)
+        # bf16 output: within one rounding of the exact value (half an ulp, 2^-9 relative) plus fp32 noise
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
+
+@pytest.mark.parametrize("offset", [1000.0, -1000.0, 80.0])
+def test_softmax_large_offsets(rf_gpu, offset):
+    """exp(x) alone overflows here even in fp64; only the max-shifted form survives."""
+    r = W.rng(101, int(abs(offset)))
+    x = (r.standard_normal((8, 5000)) * 2 + offset).astype(np.float32)
+    note(f"softmax offset {offset}")
+    y = rf_gpu.rf_softmax_rows(dev_f32(x))
+    assert_close(host_f64(y), O.softmax_rows(x), 1e-5, "softmax offset")
+
+
+def test_softmax_special_values(rf_gpu):
+    x = np.zeros((4, 300), np.float32)
+    x[0] = -np.inf                       # all -inf: NaN, as the definition gives
+    x[1, ::2] = -np.inf                  # half masked
+    x[2, 7] = 5.0
+    x[2, 100:] = -np.inf
+    x[3] = np.linspace(-30, 30, 300)
+    note("softmax special values")
+    y = host_f64(rf_gpu.rf_softmax_rows(dev_f32(x)))
+    assert np.isnan(y[0]).all()
+    with np.errstate(invalid="ignore"):
+        ref = O.softmax_rows(x[1:])
+    assert_close(y[1:], ref, 1e-6, "softmax special")
+
+
+def test_softmax_deterministic(rf_gpu):
+    x = dev_f32(W.softmax_rows_input(2, 16, 32768))
+    note("softmax determinism")
+    a = rf_gpu.rf_softmax_rows(x)
+    b = rf_gpu.rf_softmax_rows(x)
+    assert bool((a == b).all())
+
+
+# ---------------------------------------------------------------------------
+# LSE merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,S,d", [(1, 1, 1), (7, 3, 5), (64, 16, 128), (33, 5, 64), (10, 1024, 4), (5, 2, 130)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_lse_merge(rf_gpu, n, S, d, out):
+    import torch
+    r = W.rng(102, n, S, d)
+    o_parts = r.standard_normal((n, S, d)).astype(np.float32)
+    lse_parts = (r.standard_normal((n, S)) * 3 + r.uniform(-20, 20, (n, 1))).astype(np.float32)
+    dead = r.uniform(size=(n, S)) < 0.25
+    lse_parts[dead] = -np.inf
+    o_parts[dead] = np.nan                 # must never be read
+    lse_parts[0] = -np.inf                 # a row with no live part
+    note(f"lse_merge n={n} S={S} d={d} out={out}")
+    o, lse = rf_gpu.rf_lse_merge(dev_f32(o_parts), dev_f32(lse_parts),
+                                 out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    ref_o, ref_lse = O.lse_merge(np.where(dead[..., None], 0.0, o_parts), lse_parts)
+    assert_close(host_f64(o), ref_o, 1e-5 if out == "f32" else 1e-2, "merged O")
+    assert_close(host_f64(lse), ref_lse, 1e-5, "merged LSE")
+
+
+# ---------------------------------------------------------------------------
+# split-KV decode
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [  # B, H, Lk, d, splits
+    (1, 1, 1, 128, 1), (2, 3, 100, 128, 3), (2, 2, 37, 64, 16), (1, 2, 4096, 128, 16),
+    (2, 1, 5000, 64, 7), (1, 1, 33, 128, 64), (3, 2, 2048, 128, 1), (1, 1, 0, 128, 4),
+]
+
+
+@pytest.mark.parametrize("B,H,Lk,d,S", DECODE_CASES)
+def test_decode_splitkv(rf_gpu, B, H, Lk, d, S):
+    q = _normal(103, 0, (B, H, 1, d), "bf16")
+    k = _normal(103, 1, (B, H, Lk, d), "bf16")
+    v = _normal(103, 2, (B, H, Lk, d), "bf16")
+    scale = 1 / math.sqrt(d)
+    note(f"decode B={B} H={H} Lk={Lk} d={d} S={S}")
+    o, lse = rf_gpu.rf_attention_decode_splitkv(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, num_splits=S)
+    ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(q), O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v), scale)
+    assert_close(host_f64(o), ref_o, 1e-2, "decode O")
+    assert_close(host_f64(lse), ref_lse[:, :, 0], 1e-3, "decode LSE")
+
+
+def test_decode_workspace_fully_written(rf_gpu):
+    """NaN-filled workspace: every partial must be overwritten (else NaN leaks out)."""
+    import torch
+    B, H, Lk, d, S = 2, 2, 1000, 128, 16
+    q, k, v = (_normal(104, i, (B, H, L, d), "bf16") for i, L in ((0, 1), (1, Lk), (2, Lk)))
+    ws = torch.full((rf_gpu.rf_attention_decode_splitkv_workspace_size(B, H, d, S) // 4,), float("nan"),
+                    device="cuda")
+    note("decode NaN workspace")
+    o, lse = rf_gpu.rf_attention_decode_splitkv(dev_bf16(q), dev_bf16(k), dev_bf16(v), num_splits=S,
+                                                workspace=ws.view(torch.uint8))
+    ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(q), O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v),
+                                 1 / math.sqrt(d))
+    assert_close(host_f64(o), ref_o, 1e-2, "decode O")
+    assert_close(host_f64(lse), ref_lse[:, :, 0], 1e-3, "decode LSE")
+
+
+# ---------------------------------------------------------------------------
+# attention forward (fp32 and bf16)
+# ---------------------------------------------------------------------------
+
+ATT_CASES = [  # B, H, Lq, Lk, causal, mask density (None = dense)
+    (1, 1, 1, 1, False, None), (1, 2, 64, 64, False, None), (2, 2, 200, 200, True, None),
+    (1, 1, 300, 257, True, None), (1, 2, 100, 300, True, None), (1, 1, 300, 100, True, None),
+    (1, 1, 130, 77, False, None), (2, 1, 256, 256, True, 0.5), (1, 2, 333, 321, False, 0.4),
+    (1, 1, 192, 448, True, 0.3), (1, 1, 64, 0, False, None), (1, 3, 513, 513, True, None),
+]
+
+
+def _mask(seed, Lq, Lk, density):
+    if density is None:
+        return None
+    r = W.rng(seed, 4, Lq, Lk)
+    m = (r.uniform(size=(math.ceil(Lq / 64), math.ceil(Lk / 64))) < density).astype(np.uint8)
+    m[0, 0] = 1
+    return m
+
+
+def _check_attention(rf_gpu, dtype, d, B, H, Lq, Lk, causal, density, seed, tol_o):
+    import torch
+    q = _normal(seed, 0, (B, H, Lq, d), dtype)
+    k = _normal(seed, 1, (B, H, Lk, d), dtype)
+    v = _normal(seed, 2, (B, H, Lk, d), dtype)
+    bm = _mask(seed, Lq, Lk, density)
+    scale = 1 / math.sqrt(d)
+    note(f"attention {dtype} d={d} B={B} H={H} Lq={Lq} Lk={Lk} causal={causal} mask={density}")
+    o, lse = rf_gpu.rf_attention_fwd(_dev(q, dtype), _dev(k, dtype), _dev(v, dtype), scale=scale, causal=causal,
+                                     block_mask=None if bm is None else torch.from_numpy(bm).cuda())
+    ref_o, ref_lse = O.attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale, causal, bm)
+    e_o = assert_close(host_f64(o), ref_o, tol_o, "O")
+    e_l = assert_close(host_f64(lse), ref_lse, 1e-3 if dtype == "bf16" else 1e-5, "LSE")
+    return e_o, e_l
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,causal,density", ATT_CASES)
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_bf16(rf_gpu, d, B, H, Lq, Lk, causal, density):
+    _check_attention(rf_gpu, "bf16", d, B, H, Lq, Lk, causal, density, 105, 1e-2)
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,causal,density", ATT_CASES)
+@pytest.mark.parametrize("d", [1, 17, 64, 100, 128])
+def test_attention_f32(rf_gpu, d, B, H, Lq, Lk, causal, density):
+    _check_attention(rf_gpu, "f32", d, B, H, Lq, Lk, causal, density, 106, 1e-5)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_scale_sign_and_zero(rf_gpu, dtype):
+    for scale in (-0.3, 0.0, 2.5):
+        q = _normal(107, 0, (1, 2, 150, 64), dtype)
+        k = _normal(107, 1, (1, 2, 130, 64), dtype)
+        v = _normal(107, 2, (1, 2, 130, 64), dtype)
+        note(f"attention {dtype} scale={scale}")
+        o, lse = rf_gpu.rf_attention_fwd(_dev(q, dtype), _dev(k, dtype), _dev(v, dtype), scale=scale, causal=True)
+        ref_o, ref_lse = O.attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), scale, True)
+        # fp32: the rounding of the d-term dot product puts about |s| 2^-24 sqrt(d) into each
+        # exponent argument, and |s| grows like |scale| sqrt(d); the 1e-5 gate is the case
+        # |scale| sqrt(d) <= 1 (the configured 1/sqrt(d) scaling) and widens in proportion.
+        tol32 = 1e-5 * max(1.0, abs(scale) * math.sqrt(64))
+        assert_close(host_f64(o), ref_o, 1e-2 if dtype == "bf16" else tol32, f"O scale={scale}")
+        assert_close(host_f64(lse), ref_lse, 1e-3 if dtype == "bf16" else tol32, f"LSE scale={scale}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_tiles_are_skipped_not_reset(rf_gpu, dtype):
+    """NaN-poison every K/V row of key tiles that no query row may see: the
+    output must stay finite and exact, so those tiles were never loaded."""
+    import torch
+    B, H, L, d = 1, 2, 512, 64
+    q = _normal(108, 0, (B, H, L, d), dtype)
+    k = _normal(108, 1, (B, H, L, d), dtype)
+    v = _normal(108, 2, (B, H, L, d), dtype)
+    bm = np.tril(np.ones((8, 8), np.uint8))
+    bm[:, 2] = 0
+    bm[:, 5] = 0
+    ref_o, ref_lse = O.attention(_widen(q, dtype), _widen(k, dtype), _widen(v, dtype), 0.125, True, bm)
+    kp, vp = k.copy(), v.copy()
+    nan = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    for tile in (2, 5):
+        kp[:, :, tile * 64:(tile + 1) * 64] = nan
+        vp[:, :, tile * 64:(tile + 1) * 64] = nan
+    note(f"NaN-poisoned masked tiles {dtype}")
+    o, lse = rf_gpu.rf_attention_fwd(_dev(q, dtype), _dev(kp, dtype), _dev(vp, dtype), scale=0.125, causal=True,
+                                     block_mask=torch.from_numpy(bm).cuda())
+    assert_close(host_f64(o), ref_o, 1e-2 if dtype == "bf16" else 1e-5, "O")
+    assert_close(host_f64(lse), ref_lse, 1e-3 if dtype == "bf16" else 1e-5, "LSE")
+
+
+def test_attention_bf16_rising_scores(rf_gpu):
+    """Scores that rise along the keys move the running max in every tile."""
+    d, L = 128, 640
+    q = np.ones((1, 1, L, d), np.float32) * 0.1
+    k = (np.linspace(0, 4, L)[:, None] * np.ones((1, d))).astype(np.float32)[None, None]
+    v = _normal(109, 2, (1, 1, L, d), "f32")
+    qb, kb, vb = (W.f32_to_bf16_bits(a) for a in (q, k, v))
+    note("rising scores")
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), causal=True)
+    ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a) for a in (qb, kb, vb)), 1 / math.sqrt(d), True)
+    assert_close(host_f64(o), ref_o, 1e-2, "O")
+    assert_close(host_f64(lse), ref_lse, 1e-3, "LSE")
+
+
+def test_attention_bf16_deterministic(rf_gpu):
+    q, k, v = (dev_bf16(_normal(110, i, (2, 4, 700, 128), "bf16")) for i in range(3))
+    note("attention determinism")
+    o1, l1 = rf_gpu.rf_attention_fwd(q, k, v, causal=True)
+    o2, l2 = rf_gpu.rf_attention_fwd(q, k, v, causal=True)
+    assert bool((o1.view(dtype=__import__("torch").int16) == o2.view(dtype=__import__("torch").int16)).all())
+    assert bool((l1 == l2).all())
+
+
+def test_output_canaries(rf_gpu):
+    """Writes stay inside the outputs: guard regions around O and LSE keep their bytes."""
+    import torch
+    B, H, Lq, Lk, d = 1, 2, 200, 190, 128
+    q, k, v = (dev_bf16(_normal(111, i, (B, H, L, d), "bf16")) for i, L in ((0, Lq), (1, Lk), (2, Lk)))
+    pad = 4096
+    ob = torch.full((pad + B * H * Lq * d + pad,), 12345, dtype=torch.int16, device="cuda")
+    lb = torch.full((pad + B * H * Lq + pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = ob[pad:pad + B * H * Lq * d].view(torch.bfloat16).view(B, H, Lq, d)
+    lse = lb[pad:pad + B * H * Lq].view(B, H, Lq)
+    note("canaries")
+    rf_gpu.rf_attention_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((ob[:pad] == 12345).all()) and bool((ob[-pad:] == 12345).all())
+    assert bool((lb[:pad] == 7.0).all()) and bool((lb[-pad:] == 7.0).all())

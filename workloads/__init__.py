@@ -62,13 +62,16 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Input preparation only: the draws are float32, the bf16 workloads store
     the rounded bit patterns, and both sides widen those bits themselves.
     """
-    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
-    out = ((b + bias) >> np.uint32(16)).astype(np.uint16)
-    nan = np.isnan(x)
+    b = np.array(x, dtype=np.float32, copy=True).reshape(-1).view(np.uint32)
+    nan = np.isnan(b.view(np.float32))
+    t = b >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    b += t
+    out = b.view(np.uint16)[1::2].copy()       # little-endian: the high half of each word
     if nan.any():
         out[nan] = np.uint16(0x7FC0)
-    return out
+    return out.reshape(np.shape(x))
 
 
 def normal_head(seed: int, tensor_id: int, b: int, h: int, L: int, d: int, dtype: str) -> np.ndarray:
@@ -77,51 +80,50 @@ def normal_head(seed: int, tensor_id: int, b: int, h: int, L: int, d: int, dtype
     return f32_to_bf16_bits(z) if dtype == "bf16" else z
 
 
+_SHARED = {}
+
+
 def _fill_heads(args):
-    seed, tensor_id, B, H, L, d, dtype, shm_name, lo, hi = args
-    from multiprocessing import shared_memory
-    shm = shared_memory.SharedMemory(name=shm_name)
-    try:
-        npdt = np.uint16 if dtype == "bf16" else np.float32
-        arr = np.ndarray((B * H, L, d), dtype=npdt, buffer=shm.buf)
-        for bh in range(lo, hi):
-            arr[bh] = normal_head(seed, tensor_id, bh // H, bh % H, L, d, dtype)
-        del arr
-    finally:
-        shm.close()
+    key, seed, tensor_id, B, H, L, d, dtype, lo, hi = args
+    arr = _SHARED[key]
+    for bh in range(lo, hi):
+        arr[bh] = normal_head(seed, tensor_id, bh // H, bh % H, L, d, dtype)
     return hi - lo
 
 
 def normal_tensor(seed: int, tensor_id: int, B: int, H: int, L: int, d: int, dtype: str,
                   workers: int | None = None) -> np.ndarray:
-    """A [B, H, L, d] tensor assembled from per-head draws (parallel for large tensors)."""
+    """A [B, H, L, d] tensor assembled from per-head draws.
+
+    Large tensors are filled by a pool of forked workers writing straight into
+    an anonymous shared mapping, which the returned array keeps alive (no copy).
+    """
     npdt = np.uint16 if dtype == "bf16" else np.float32
     n_heads = B * H
     nbytes = n_heads * L * d * np.dtype(npdt).itemsize
     if workers is None:
         workers = min(16, len(os.sched_getaffinity(0)))
-    if nbytes < (256 << 20) or workers <= 1:
+    if nbytes < (64 << 20) or workers <= 1 or n_heads < 2:
         out = np.empty((n_heads, L, d), dtype=npdt)
         for bh in range(n_heads):
             out[bh] = normal_head(seed, tensor_id, bh // H, bh % H, L, d, dtype)
         return out.reshape(B, H, L, d)
-    from multiprocessing import get_context, shared_memory
-    shm = shared_memory.SharedMemory(create=True, size=nbytes)
+    import mmap
+    from multiprocessing import get_context
+    mm = mmap.mmap(-1, nbytes, flags=mmap.MAP_SHARED | mmap.MAP_ANONYMOUS)
+    arr = np.frombuffer(mm, dtype=npdt).reshape(n_heads, L, d)
+    key = id(arr)
+    _SHARED[key] = arr          # inherited by the forked workers
     try:
-        step = max(1, math.ceil(n_heads / (workers * 4)))
-        jobs = [(seed, tensor_id, B, H, L, d, dtype, shm.name, lo, min(n_heads, lo + step))
+        step = max(1, math.ceil(n_heads / (workers * 8)))
+        jobs = [(key, seed, tensor_id, B, H, L, d, dtype, lo, min(n_heads, lo + step))
                 for lo in range(0, n_heads, step)]
         with ProcessPoolExecutor(max_workers=workers, mp_context=get_context("fork")) as ex:
             done = sum(ex.map(_fill_heads, jobs))
         assert done == n_heads
-        view = np.ndarray((B, H, L, d), dtype=npdt, buffer=shm.buf)
-        out = np.empty_like(view)
-        np.copyto(out, view)
-        del view
-        return out
     finally:
-        shm.close()
-        shm.unlink()
+        del _SHARED[key]
+    return arr.reshape(B, H, L, d)
 
 
 def softmax_row(seed: int, r: int, cols: int) -> np.ndarray:
