@@ -96,7 +96,8 @@ int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtyp
  *                One mask is shared by all (b, h). Masked tiles are skipped.
  * Visible(i, j) = causal rule AND block rule AND j < Lk. A query row with no
  * visible key gets O = 0 and LSE = -inf.
- * Supported: RF_BF16 with d in {64, 128}; RF_F32 with 1 <= d <= 128.
+ * Supported: RF_BF16 with d in {64, 128} and Lk * d * 2 < 2^31 (bytes of one
+ * head's K); RF_F32 with 1 <= d <= 128.
  * B, H, Lq, Lk >= 0 (any of B, H, Lq zero enqueues nothing).
  * Errors: RF_ERR_INVALID_ARG (NULL pointers when work exists, negative sizes,
  * non-finite scale, unknown dtype), RF_ERR_UNSUPPORTED (other d), RF_ERR_HIP.

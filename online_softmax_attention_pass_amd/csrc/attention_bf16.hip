@@ -36,8 +36,25 @@
 namespace rf {
 namespace {
 
+// Launch shape per head dim: waves per workgroup (32 query rows each) and
+// waves per SIMD the register allocation must allow.
+#ifndef RF_ATT_NW_D128
+#define RF_ATT_NW_D128 4
+#endif
+#ifndef RF_ATT_WPE_D128
+#define RF_ATT_WPE_D128 2
+#endif
+#ifndef RF_ATT_NW_D64
+#define RF_ATT_NW_D64 2
+#endif
+#ifndef RF_ATT_WPE_D64
+#define RF_ATT_WPE_D64 2
+#endif
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBN = 64;        // keys per tile
 constexpr int kMaskTile = 64;  // block-mask granularity
@@ -57,34 +74,34 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Position of key kappa (0..15) inside a 16-key group of a V^T row: the MFMA
-// K-slot that the S^T accumulator layout assigns to it (key quads 1 and 2 swap).
-__device__ __forceinline__ int vt_quad_pos(int quad) { return ((quad & 1) << 1) | (quad >> 1); }
+// Raw buffer access: loads outside [0, bytes) return zero, so ragged tiles
+// need no predication.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
-template <int D, int NW>
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte rows supplied by lanes i/4,
+// i/4 + 4, i/4 + 8, i/4 + 12 of its group.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(reinterpret_cast<uintptr_t>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int D>
 struct Smem {
-  static constexpr int KROW = D + 8;      // padded K row (bf16): conflict-free 16-byte reads
-  static constexpr int VROW = kBN + 8;    // padded V^T row (bf16)
+  static constexpr int KROW = D + 8;      // K row stride (bf16): 16-byte pad, conflict-free b128 reads
+  static constexpr int VROW = D + 16;     // V row stride (bf16): 32-byte pad, conflict-free transposed reads
   static constexpr int K_ELEMS = kBN * KROW;
-  static constexpr int V_ELEMS = D * VROW;
+  static constexpr int V_ELEMS = kBN * VROW;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
   static constexpr int BYTES = 2 * BUF_ELEMS * 2;
 };
-
-// Per-item description shared by all waves.
-struct Item {
-  int64_t bh;
-  int q0;
-};
-
-template <int D, int NW>
-__device__ __forceinline__ Item item_of(int64_t item, int n_qt, bool heavy_first) {
-  Item it;
-  it.bh = item / n_qt;
-  const int r = int(item % n_qt);
-  it.q0 = (heavy_first ? (n_qt - 1 - r) : r) * (32 * NW);
-  return it;
-}
 
 // Is key tile kt visible to any of the workgroup's mask rows?
 __device__ __forceinline__ bool tile_active(const uint8_t* __restrict__ mask, int n_mask_cols, int mr0, int mr1,
@@ -96,21 +113,19 @@ __device__ __forceinline__ bool tile_active(const uint8_t* __restrict__ mask, in
   return a;
 }
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
+template <int D, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
     const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap) {
-  using S = Smem<D, NW>;
+  using S = Smem<D>;
   constexpr int NT = NW * 64;
   constexpr int BM = 32 * NW;
-  constexpr int KCH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int KSTEPS = D / 16;      // MFMA K-steps for S^T
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
-  constexpr int K_LD = kBN * KCH / NT;  // K chunks per thread per tile
-  constexpr int V_ITEMS = 16 * KCH;      // (key quad, d chunk) items per tile
-  constexpr int V_LD = (V_ITEMS + NT - 1) / NT;
-  static_assert(kBN * KCH % NT == 0, "K tile split");
+  constexpr int KCH = D / 8;            // 16-byte chunks per K/V row
+  constexpr int KSTEPS = D / 16;        // MFMA K-steps for S^T
+  constexpr int DB = D / 32;            // 32-row blocks of O^T
+  constexpr int LD = kBN * KCH / NT;    // chunks per thread per tile, for K and for V
+  static_assert(kBN * KCH % NT == 0, "tile split");
 
   extern __shared__ __align__(16) uint16_t smem[];
 
@@ -119,21 +134,38 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
   const int lane = t & 63;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int off = Lk - Lq;  // bottom-right causal alignment: key j visible to row i iff j <= i + off
-  const int n_kt = (Lk + kBN - 1) / kBN;
+  const int64_t off = int64_t(Lk) - Lq;  // bottom-right causal alignment: key j visible to row i iff j <= i + off
   const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
   const int64_t per_xcd = n_items / 8;
+  const uint32_t head_bytes = uint32_t(Lk) * D * 2;
+
+  // Per-thread parts of the tile addressing (constant over the sweep).
+  uint32_t ld_goff[LD];
+  int ld_soff[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    const int idx = t + i * NT;
+    const int row = idx / KCH, c = idx % KCH;
+    ld_goff[i] = uint32_t(row * D * 2 + 16 * c);
+    ld_soff[i] = row * S::KROW + 8 * c;  // K offset; V uses row * VROW + 8 c
+  }
+  // Transposed V^T fragment addressing (see lds_read_tr16): this lane supplies
+  // row 4 h + (lane % 16) / 4 (+ 8 for the second half) and column
+  // 16 ((lane / 16) % 2) + 4 (lane % 4) of each 16-key, 32-column block.
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   for (int64_t g = blockIdx.x; g < n_items; g += gridDim.x) {
     // XCD-aware placement: consecutive workgroups land on consecutive XCDs, so
     // give each XCD a contiguous range of items (whole heads, tiles in order).
     const int64_t item = xcd_remap ? (g % 8) * per_xcd + g / 8 : g;
-    const Item it = item_of<D, NW>(item, n_qt, causal != 0);
-    const int q0 = it.q0;
+    const int64_t bh = item / n_qt;
+    const int qr = int(item % n_qt);
+    const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;  // heaviest causal tiles first
     const int q0w = q0 + 32 * wave;
-    const uint16_t* qh = q + it.bh * int64_t(Lq) * D;
-    const uint16_t* kh = k + it.bh * int64_t(Lk) * D;
-    const uint16_t* vh = v + it.bh * int64_t(Lk) * D;
+    const uint16_t* qh = q + bh * int64_t(Lq) * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + bh * int64_t(Lk) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + bh * int64_t(Lk) * D, head_bytes);
 
     // Key tiles this workgroup may need: [0, kt_end), minus masked tiles.
     int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
@@ -166,68 +198,31 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-    float m_run = kNegInf;  // running max of this lane's query row (log2 units)
+    float m_ref = kNegInf;  // running max of this lane's query row (log2 units)
     float l_run = 0.f;      // this lane's share of the running sum (lane l ^ 32 holds the rest)
+    // Last visible key of this lane's row, relative to tile start k0 and to the
+    // lane's key offset 4 h (the register pattern adds 32 mb + 8 (r/4) + r%4).
+    const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
+    const int row_lim = int(row_last < int64_t(Lk) - 1 ? (row_last < -1 ? -1 : row_last) : int64_t(Lk) - 1);
 
-    // Global -> register staging of one K/V tile.
-    uint4 kst[K_LD];
-    uint4 vst[V_LD][4];
+    uint4 kst[LD], vst[LD];
     auto load_tile = [&](int kt) {
-      const int k0 = kt * kBN;
+      const uint32_t base = uint32_t(kt) * kBN * D * 2;
 #pragma unroll
-      for (int i = 0; i < K_LD; ++i) {
-        const int idx = t + i * NT;
-        const int row = idx / KCH, c = idx % KCH;
-        kst[i] = (k0 + row < Lk) ? *reinterpret_cast<const uint4*>(kh + int64_t(k0 + row) * D + 8 * c)
-                                 : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < V_LD; ++i) {
-        const int idx = t + i * NT;
-        if (idx < V_ITEMS) {
-          const int quad = idx % 16, c = idx / 16;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = k0 + 4 * quad + j;
-            vst[i][j] = (key < Lk) ? *reinterpret_cast<const uint4*>(vh + int64_t(key) * D + 8 * c)
-                                   : make_uint4(0, 0, 0, 0);
-          }
-        }
+      for (int i = 0; i < LD; ++i) {
+        kst[i] = buf_load16(krs, base + ld_goff[i]);
+        vst[i] = buf_load16(vrs, base + ld_goff[i]);
       }
     };
     auto store_tile = [&](int buf) {
       uint16_t* ks_ = smem + buf * S::BUF_ELEMS;
       uint16_t* vs_ = ks_ + S::K_ELEMS;
 #pragma unroll
-      for (int i = 0; i < K_LD; ++i) {
+      for (int i = 0; i < LD; ++i) {
         const int idx = t + i * NT;
         const int row = idx / KCH, c = idx % KCH;
-        *reinterpret_cast<uint4*>(ks_ + row * S::KROW + 8 * c) = kst[i];
-      }
-#pragma unroll
-      for (int i = 0; i < V_LD; ++i) {
-        const int idx = t + i * NT;
-        if (idx < V_ITEMS) {
-          const int quad = idx % 16, c = idx / 16;
-          const int pos = 16 * (quad >> 2) + 4 * vt_quad_pos(quad & 3);
-          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vst[i][0]);
-          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vst[i][1]);
-          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vst[i][2]);
-          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vst[i][3]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            uint2 col;
-            if (e & 1) {
-              col.x = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
-              col.y = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
-            } else {
-              col.x = (w0[w] & 0xffffu) | (w1[w] << 16);
-              col.y = (w2[w] & 0xffffu) | (w3[w] << 16);
-            }
-            *reinterpret_cast<uint2*>(vs_ + (8 * c + e) * S::VROW + pos) = col;
-          }
-        }
+        *reinterpret_cast<uint4*>(ks_ + ld_soff[i]) = kst[i];
+        *reinterpret_cast<uint4*>(vs_ + row * S::VROW + 8 * c) = vst[i];
       }
     };
 
@@ -266,15 +261,12 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
         // ---- element mask, only where the tile straddles the diagonal or the key end ----
         const bool edge = (causal && int64_t(k0) + kBN - 1 > int64_t(q0w) + off) || (k0 + kBN > Lk);
         if (edge) {
-          const int64_t lim = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
-          const int64_t kmax = lim < Lk - 1 ? lim : int64_t(Lk) - 1;
+          const int lim = row_lim - k0 - 4 * h;
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-              if (key > kmax) st[mb][r] = kNegInf;
-            }
+            for (int r = 0; r < 16; ++r)
+              if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
         }
         // ---- online softmax update (log2 units) ----
         float mx = kNegInf;
@@ -283,11 +275,21 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
         mx = fmaxf(mx, shfl_xor(mx, 32));  // lane l ^ 32 holds the other 32 keys of the row
-        const float m_new = fmaxf(m_run, mx * c_log2);
-        const float mu = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - mu);
-        m_run = m_new;
-        float psum = 0.f;
+        // The reference is the exact running max, so the row's largest weight is
+        // exactly 1 and carries no bf16 rounding into O. The accumulator is
+        // rescaled only on tiles where some row's max moved (wave-uniform branch).
+        const float mt = mx * c_log2;
+        const bool move = mt > m_ref;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+          const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;
+          if (move) m_ref = mt;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+        }
+        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
         uint32_t pk[2][8];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -295,25 +297,20 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
           for (int r = 0; r < 16; r += 2) {
             const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
             const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
-            psum += p0 + p1;
+            l_run += p0 + p1;
             pk[mb][r >> 1] = cvt_pk_bf16(p0, p1);
           }
-        l_run = l_run * alpha + psum;
-        if (alpha != 1.f) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-        }
         // ---- O^T += V^T P^T ----
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int mb = ks >> 1, r0 = (ks & 1) * 4;
           const uint4 bp = make_uint4(pk[mb][r0], pk[mb][r0 + 1], pk[mb][r0 + 2], pk[mb][r0 + 3]);
+          const uint16_t* vrow = vs_ + (16 * ks + tr_row) * S::VROW + tr_col;
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint4 a = *reinterpret_cast<const uint4*>(vs_ + (32 * db + l32) * S::VROW + 16 * ks + 8 * h);
-            acc_o[db] = mfma32(as_bf16x8(a), as_bf16x8(bp), acc_o[db]);
+            const uint2 lo = lds_read_tr16(vrow + 32 * db);
+            const uint2 hi = lds_read_tr16(vrow + 8 * S::VROW + 32 * db);
+            acc_o[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(bp), acc_o[db]);
           }
         }
       }
@@ -330,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
     if (qi < Lq) {
       const bool live = l_tot > 0.f;
       const float inv = live ? 1.f / l_tot : 0.f;
-      uint16_t* orow = o + (it.bh * Lq + qi) * int64_t(D);
+      uint16_t* orow = o + (bh * Lq + qi) * int64_t(D);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -341,12 +338,12 @@ __global__ __launch_bounds__(NW * 64) void attention_bf16_kernel(
           pkt.y = cvt_pk_bf16(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
           *reinterpret_cast<uint2*>(orow + d0) = pkt;
         }
-      if (lse != nullptr && h == 0) lse[it.bh * Lq + qi] = live ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+      if (lse != nullptr && h == 0) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, int WPE>
 hipError_t launch_kernel(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
                          int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
   constexpr int BM = 32 * NW;
@@ -364,13 +361,13 @@ hipError_t launch_kernel(const void* q, const void* k, const void* v, void* o, f
   const int64_t cap = 1LL << 22;
   const unsigned grid = unsigned(n_items < cap ? n_items : cap);
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
-  const size_t shmem = Smem<D, NW>::BYTES;
+  const size_t shmem = Smem<D>::BYTES;
   // One-time, thread-safe opt-in to more than 64 KiB of dynamic LDS for this instantiation.
   static const hipError_t attr_err = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&attention_bf16_kernel<D, NW>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      reinterpret_cast<const void*>(&attention_bf16_kernel<D, NW, WPE>), hipFuncAttributeMaxDynamicSharedMemorySize,
       int(shmem));
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL((attention_bf16_kernel<D, NW>), dim3(grid), dim3(NW * 64), shmem, stream,
+  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WPE>), dim3(grid), dim3(NW * 64), shmem, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
                      block_mask, n_qt, n_items, xcd_remap);
@@ -382,8 +379,11 @@ hipError_t launch_kernel(const void* q, const void* k, const void* v, void* o, f
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
                                  hipStream_t stream) {
-  if (d == 128) return launch_kernel<128, 4>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
-  return launch_kernel<64, 4>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
+  if (d == 128)
+    return launch_kernel<128, RF_ATT_NW_D128, RF_ATT_WPE_D128>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
+                                                                block_mask, stream);
+  return launch_kernel<64, RF_ATT_NW_D64, RF_ATT_WPE_D64>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask,
+                                                           stream);
 }
 
 }  // namespace rf

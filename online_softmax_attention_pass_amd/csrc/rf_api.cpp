@@ -131,6 +131,8 @@ int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float
     if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL q or o");
     if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL k or v");
     if (dtype == RF_BF16) {
+      if (int64_t(Lk) * d * 2 > INT32_MAX)
+        return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: bf16 path needs Lk * d * 2 < 2^31 bytes per head");
       if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
         return fail(RF_ERR_UNSUPPORTED,
                     "rf_attention_fwd: bf16 path needs 16-byte aligned q, k, v and 8-byte aligned o");

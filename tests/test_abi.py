@@ -102,6 +102,8 @@ def att(lib, **kw):
     (dict(B=0), OK), (dict(H=0), OK), (dict(Lq=0), OK),
     (dict(B=0, q=NUL, k=NUL, v=NUL, o=NUL), OK),
     (dict(B=1 << 20, H=1 << 20, Lq=1 << 20), INVALID),  # overflow
+    (dict(Lk=1 << 23), UNSUP),                           # one bf16 K head beyond 2^31 bytes
+    (dict(Lk=(1 << 23) - 1, B=0), OK),
 ])
 def test_attention_validation(lib, kw, code):
     assert att(lib, **kw) == code
