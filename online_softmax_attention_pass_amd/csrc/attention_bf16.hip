@@ -96,7 +96,10 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 template <int D>
 struct Smem {
   static constexpr int KROW = D + 8;      // K row stride (bf16): 16-byte pad, conflict-free b128 reads
-  static constexpr int VROW = D + 16;     // V row stride (bf16): 32-byte pad, conflict-free transposed reads
+  // V row stride (bf16): the pad shifts consecutive rows so the 4-row transposed reads
+  // of a lane group hit distinct banks (64 bytes for D = 128; 32 bytes for D = 64, which
+  // keeps four 2-wave workgroups within the 160 KiB of LDS).
+  static constexpr int VROW = D + (D >= 128 ? 32 : 16);
   static constexpr int K_ELEMS = kBN * KROW;
   static constexpr int V_ELEMS = kBN * VROW;
   static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
-        mx = fmaxf(mx, shfl_xor(mx, 32));  // lane l ^ 32 holds the other 32 keys of the row
+        mx = pair_max_halves(mx);  // lane l ^ 32 holds the other 32 keys of the row
         // The reference is the exact running max, so the row's largest weight is
         // exactly 1 and carries no bf16 rounding into O. The accumulator is
         // rescaled only on tiles where some row's max moved (wave-uniform branch).
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
 
     // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-    const float l_tot = l_run + shfl_xor(l_run, 32);
+    const float l_tot = pair_sum_halves(l_run);
     const int qi = q0w + l32;
     if (qi < Lq) {
       const bool live = l_tot > 0.f;

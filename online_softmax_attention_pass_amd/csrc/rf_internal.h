@@ -84,6 +84,18 @@ __device__ __forceinline__ float group_max(float x) {
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Max / sum of a value over the lane pair (l, l ^ 32), via v_permlane32_swap:
+// the two results hold the low half and the high half of x broadcast across
+// the wavefront, so combining them symmetrically needs no LDS round trip.
+__device__ __forceinline__ float pair_max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // The (m, l) pair of a partial safe-softmax reduction, m in log2 units:
 // (m_a, l_a) (+) (m_b, l_b) = (M, l_a 2^(m_a - M) + l_b 2^(m_b - M)), M = max.
 // The identity is (-inf, 0); combining two identities stays the identity.
