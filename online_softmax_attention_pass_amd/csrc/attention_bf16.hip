@@ -47,6 +47,9 @@ namespace {
 #ifndef RF_ATT_NW_D64
 #define RF_ATT_NW_D64 2
 #endif
+#ifndef RF_ATT_PINGPONG_D128
+#define RF_ATT_PINGPONG_D128 0
+#endif
 #ifndef RF_ATT_WPE_D64
 #define RF_ATT_WPE_D64 2
 #endif
@@ -73,6 +76,21 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   v[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, v);
 }
+
+// Sum of the two bf16 halves of a packed pair, accumulated in fp32.
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
+                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+}
+
+// Lazy rescale: a row's exponent reference moves only when a tile's max exceeds
+// it by more than kRescaleSlack (log2 units), so almost every tile skips the
+// accumulator rescale. The weights p = 2^(t - m_ref) then stay <= 2^8 but the
+// largest is no longer exactly 1 in bf16, so O is normalised by the sum of the
+// same rounded weights the MFMA consumed (O stays an exact convex combination of
+// V rows), while the LSE uses the sum of the unrounded weights.
+constexpr float kRescaleSlack = 8.f;
 
 // Raw buffer access: loads outside [0, bytes) return zero, so ragged tiles
 // need no predication.
@@ -106,15 +124,58 @@ struct Smem {
   static constexpr int BYTES = 2 * BUF_ELEMS * 2;
 };
 
-// Is key tile kt visible to any of the workgroup's mask rows?
-__device__ __forceinline__ bool tile_active(const uint8_t* __restrict__ mask, int n_mask_cols, int mr0, int mr1,
-                                            int kt) {
-  if (mask == nullptr) return true;
-  const int mc = (kt * kBN) / kMaskTile;
-  bool a = false;
-  for (int mr = mr0; mr <= mr1; ++mr) a |= mask[int64_t(mr) * n_mask_cols + mc] != 0;
-  return a;
-}
+// Compiler-level pin: keeps the prefetch loads issued above it from being sunk
+// next to their use (which would turn the prefetch into a synchronous wait).
+__device__ __forceinline__ void pin_memory_order() { asm volatile("" ::: "memory"); }
+
+// Walks the key tiles a workgroup must visit, in order. Without a block mask it
+// is every tile below kt_end. With one, the mask bytes of the next 64 tiles are
+// read once per 64 tiles (one byte per lane) and turned into two wave-uniform
+// 64-bit words by ballot: tiles active for any of the workgroup's mask rows, and
+// tiles active for this wave's own mask row. The scan itself is scalar bit work.
+struct TileWalker {
+  const uint8_t* mask;
+  int n_mask_cols, mr0, mr1, mr_w, kt_end;
+  int base = -64;
+  uint64_t wg_bits = 0, wv_bits = 0;
+
+  __device__ void refill(int b) {
+    const int kt = b + int(threadIdx.x & 63);
+    bool any = false, mine = false;
+    if (kt < kt_end) {
+      const int mc = kt * kBN / kMaskTile;
+      for (int mr = mr0; mr <= mr1; ++mr) {
+        const bool a = mask[int64_t(mr) * n_mask_cols + mc] != 0;
+        any |= a;
+        mine |= (mr == mr_w) && a;
+      }
+    }
+    wg_bits = __builtin_amdgcn_ballot_w64(any);
+    wv_bits = __builtin_amdgcn_ballot_w64(mine);
+    base = b;
+  }
+  // First tile >= kt that the workgroup must visit (kt_end if none); *mine says
+  // whether this wave's mask row has it.
+  __device__ int next(int kt, bool* mine) {
+    if (mask == nullptr) {
+      *mine = true;
+      return kt < kt_end ? kt : kt_end;
+    }
+    while (kt < kt_end) {
+      if (kt < base || kt >= base + 64) refill(kt & ~63);
+      const uint64_t rest = wg_bits >> (kt - base);
+      if (rest) {
+        kt += int(__builtin_ctzll(rest));
+        if (kt >= kt_end) break;
+        *mine = (wv_bits >> (kt - base)) & 1;
+        return kt;
+      }
+      kt = base + 64;
+    }
+    *mine = false;
+    return kt_end;
+  }
+};
 
 template <int D, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_kernel(
@@ -174,13 +235,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
     if (last_key > Lk - 1) last_key = Lk - 1;
     const int kt_end = last_key < 0 ? 0 : int(last_key / kBN) + 1;
-    const int mr0 = q0 / kMaskTile;
-    const int mr1 = min(q0 + BM - 1, Lq - 1) / kMaskTile;
-    const int mr_w = min(q0w, Lq - 1) / kMaskTile;
-    auto next_tile = [&](int kt) {
-      while (kt < kt_end && !tile_active(block_mask, n_mask_cols, mr0, mr1, kt)) ++kt;
-      return kt;
-    };
+    TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+                    min(q0w, Lq - 1) / kMaskTile, kt_end};
 
     // Q^T fragments (B operand of S^T): lane holds row q0w + l32, d = 16 ks + 8 h .. + 8.
     uint4 qf[KSTEPS];
@@ -194,6 +250,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
         qf[ks] = x;
       }
+      // The Q fragments are complete before the sweep, so the loop's waits only
+      // ever concern the tile prefetches.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
     f32x16_t acc_o[DB];
@@ -201,8 +260,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-    float m_ref = kNegInf;  // running max of this lane's query row (log2 units)
-    float l_run = 0.f;      // this lane's share of the running sum (lane l ^ 32 holds the rest)
+    float m_ref = kNegInf;  // exponent reference of this lane's query row (log2 units)
+    float l_run = 0.f;      // this lane's share of the sum of weights (lane l ^ 32 holds the rest)
+    float l_rnd = 0.f;      // the same sum over the bf16-rounded weights
     // Last visible key of this lane's row, relative to tile start k0 and to the
     // lane's key offset 4 h (the register pattern adds 32 mb + 8 (r/4) + r%4).
     const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
@@ -230,7 +290,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     };
 
     __syncthreads();  // the previous item's last readers of both buffers are done
-    int kt = next_tile(0);
+    bool mine = false;
+    int kt = walk.next(0, &mine);
     int buf = 0;
     if (kt < kt_end) {
       load_tile(kt);
@@ -239,18 +300,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     __syncthreads();
 
     while (kt < kt_end) {
-      const int kt_next = next_tile(kt + 1);
-      if (kt_next < kt_end) load_tile(kt_next);  // in flight during this tile's math
+      bool mine_next = false;
+      const int kt_next = walk.next(kt + 1, &mine_next);
 
       const int k0 = kt * kBN;
-      const bool wave_visible =
-          (!causal || int64_t(k0) <= int64_t(q0w) + 31 + off) && q0w < Lq &&
-          (block_mask == nullptr || block_mask[int64_t(mr_w) * n_mask_cols + k0 / kMaskTile] != 0);
+      const bool wave_visible = (!causal || int64_t(k0) <= int64_t(q0w) + 31 + off) && q0w < Lq && mine;
+      f32x16_t st[2];
       if (wave_visible) {
         const uint16_t* ks_ = smem + buf * S::BUF_ELEMS;
-        const uint16_t* vs_ = ks_ + S::K_ELEMS;
         // ---- S^T = K Q^T (two 32-key blocks) ----
-        f32x16_t st[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -261,6 +319,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
             st[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[ks]), st[mb]);
           }
         }
+      }
+      // The next tile's loads go out after the score MFMAs and stay in flight
+      // through the softmax and the P.V products.
+      if (kt_next < kt_end) load_tile(kt_next);
+      pin_memory_order();
+      if (wave_visible) {
+        const uint16_t* vs_ = smem + buf * S::BUF_ELEMS + S::K_ELEMS;
         // ---- element mask, only where the tile straddles the diagonal or the key end ----
         const bool edge = (causal && int64_t(k0) + kBN - 1 > int64_t(q0w) + off) || (k0 + kBN > Lk);
         if (edge) {
@@ -278,15 +343,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
         mx = pair_max_halves(mx);  // lane l ^ 32 holds the other 32 keys of the row
-        // The reference is the exact running max, so the row's largest weight is
-        // exactly 1 and carries no bf16 rounding into O. The accumulator is
-        // rescaled only on tiles where some row's max moved (wave-uniform branch).
         const float mt = mx * c_log2;
-        const bool move = mt > m_ref;
-        if (__builtin_amdgcn_ballot_w64(move)) {
+        const bool move = mt > m_ref + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(move)) {  // wave-uniform: rare after the first tile
           const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;
           if (move) m_ref = mt;
           l_run *= alpha;
+          l_rnd *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -300,8 +363,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           for (int r = 0; r < 16; r += 2) {
             const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
             const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
+            const uint32_t pp = cvt_pk_bf16(p0, p1);
             l_run += p0 + p1;
-            pk[mb][r >> 1] = cvt_pk_bf16(p0, p1);
+            l_rnd = add_bf16_pair(pp, l_rnd);
+            pk[mb][r >> 1] = pp;
           }
         // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -322,9 +387,297 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       __syncthreads();
       buf ^= 1;
       kt = kt_next;
+      mine = mine_next;
     }
 
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
+    // ---- epilogue: O = acc / sum(rounded weights), LSE = (m + log2 sum(weights)) ln 2 ----
+    const float l_tot = pair_sum_halves(l_run);
+    const float l_rtot = pair_sum_halves(l_rnd);
+    const int qi = q0w + l32;
+    if (qi < Lq) {
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_rtot : 0.f;
+      uint16_t* orow = o + (bh * Lq + qi) * int64_t(D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * db + 8 * r4 + 4 * h;
+          uint2 pkt;
+          pkt.x = cvt_pk_bf16(acc_o[db][4 * r4] * inv, acc_o[db][4 * r4 + 1] * inv);
+          pkt.y = cvt_pk_bf16(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = pkt;
+        }
+      if (lse != nullptr && h == 0) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong variant for long causal / dense sweeps (d = 128).
+//
+// Eight waves form two groups of four; each SIMD holds one wave of each group.
+// A workgroup barrier splits every key tile into two phases, and the groups
+// run one phase apart, so on every SIMD one wave issues matrix-core work while
+// the other issues the softmax's vector work:
+//
+//   phase 2n   : group A  M(n) = { O += V(n-1)^T P(n-1)^T ; S(n) = K(n) Q^T }
+//                group B  V(n-1) = softmax update of S(n-1) -> P(n-1)
+//   phase 2n+1 : group A  V(n)
+//                group B  M(n)
+//                all      K(n+1), V(n) staged registers -> LDS; issue the
+//                         global loads of K(n+2), V(n+1)
+//
+// K therefore runs one tile ahead of V: K(n) and V(n-1) are live during tile
+// n, each double-buffered. Group A owns the even 32-row blocks of the 256-row
+// query tile and group B the odd ones, so both see the same causal diagonal.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attention_bf16_pp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
+    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap) {
+  using S = Smem<D>;
+  constexpr int NT = 512;
+  constexpr int BM = 256;
+  constexpr int KCH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int LD = kBN * KCH / NT;
+  static_assert(kBN * KCH % NT == 0, "tile split");
+  // LDS: two K buffers, then two V buffers.
+  constexpr int KBUF = S::K_ELEMS, VBUF = S::V_ELEMS;
+
+  extern __shared__ __align__(16) uint16_t smem[];
+  uint16_t* const kbuf0 = smem;
+  uint16_t* const vbuf0 = smem + 2 * KBUF;
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const bool grpA = wave < 4;
+  const int rowblk = 2 * (wave & 3) + (grpA ? 0 : 1);  // 32-row block inside the 256-row tile
+  const int64_t off = int64_t(Lk) - Lq;
+  const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
+  const int64_t per_xcd = n_items / 8;
+  const uint32_t head_bytes = uint32_t(Lk) * D * 2;
+
+  uint32_t ld_goff[LD];
+  int ld_row[LD], ld_c[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    const int idx = t + i * NT;
+    ld_row[i] = idx / KCH;
+    ld_c[i] = idx % KCH;
+    ld_goff[i] = uint32_t(ld_row[i] * D * 2 + 16 * ld_c[i]);
+  }
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  for (int64_t g = blockIdx.x; g < n_items; g += gridDim.x) {
+    const int64_t item = xcd_remap ? (g % 8) * per_xcd + g / 8 : g;
+    const int64_t bh = item / n_qt;
+    const int qr = int(item % n_qt);
+    const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
+    const int q0w = q0 + 32 * rowblk;
+    const uint16_t* qh = q + bh * int64_t(Lq) * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + bh * int64_t(Lk) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + bh * int64_t(Lk) * D, head_bytes);
+
+    int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
+    if (last_key > Lk - 1) last_key = Lk - 1;
+    const int kt_end = last_key < 0 ? 0 : int(last_key / kBN) + 1;
+    TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+                    min(q0w, Lq - 1) / kMaskTile, kt_end};
+    auto visible = [&](int kt, bool mine) {
+      return (!causal || int64_t(kt) * kBN <= int64_t(q0w) + 31 + off) && q0w < Lq && mine;
+    };
+
+    uint4 qf[KSTEPS];
+    {
+      const int qi = q0w + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (qi < Lq) x = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * ks + 8 * h);
+        if (q_mode == 1) { x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u; }
+        if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
+        qf[ks] = x;
+      }
+      // The Q fragments are complete before the sweep, so the loop's waits only
+      // ever concern the tile prefetches.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    f32x16_t acc_o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+    float m_ref = kNegInf;
+    float l_run = 0.f;
+    const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
+    const int row_lim = int(row_last < int64_t(Lk) - 1 ? (row_last < -1 ? -1 : row_last) : int64_t(Lk) - 1);
+
+    f32x16_t st[2];
+    uint32_t pk[2][8];
+    uint4 kst[LD], vst[LD];
+    auto load_k = [&](int kt) {
+      const uint32_t base = uint32_t(kt) * kBN * D * 2;
+#pragma unroll
+      for (int i = 0; i < LD; ++i) kst[i] = buf_load16(krs, base + ld_goff[i]);
+    };
+    auto load_v = [&](int kt) {
+      const uint32_t base = uint32_t(kt) * kBN * D * 2;
+#pragma unroll
+      for (int i = 0; i < LD; ++i) vst[i] = buf_load16(vrs, base + ld_goff[i]);
+    };
+    auto store_k = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < LD; ++i)
+        *reinterpret_cast<uint4*>(kbuf0 + b * KBUF + ld_row[i] * S::KROW + 8 * ld_c[i]) = kst[i];
+    };
+    auto store_v = [&](int b) {
+#pragma unroll
+      for (int i = 0; i < LD; ++i)
+        *reinterpret_cast<uint4*>(vbuf0 + b * VBUF + ld_row[i] * S::VROW + 8 * ld_c[i]) = vst[i];
+    };
+
+    // Matrix-core block: O += V(prev)^T P(prev)^T, then S = K(cur) Q^T.
+    auto mblock = [&](bool do_pv, int vb, bool do_s, int kb) {
+      if (do_pv) {
+        const uint16_t* vs_ = vbuf0 + vb * VBUF;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int mb = ks >> 1, r0 = (ks & 1) * 4;
+          const uint4 bp = make_uint4(pk[mb][r0], pk[mb][r0 + 1], pk[mb][r0 + 2], pk[mb][r0 + 3]);
+          const uint16_t* vrow = vs_ + (16 * ks + tr_row) * S::VROW + tr_col;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const uint2 lo = lds_read_tr16(vrow + 32 * db);
+            const uint2 hi = lds_read_tr16(vrow + 8 * S::VROW + 32 * db);
+            acc_o[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), as_bf16x8(bp), acc_o[db]);
+          }
+        }
+      }
+      if (do_s) {
+        const uint16_t* ks_ = kbuf0 + kb * KBUF;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[mb][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4*>(ks_ + (32 * mb + l32) * S::KROW + 16 * ks + 8 * h);
+            st[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[ks]), st[mb]);
+          }
+        }
+      }
+    };
+    // Vector block: online softmax update of S(kt) into P.
+    auto vblock = [&](int kt) {
+      const int k0 = kt * kBN;
+      const bool edge = (causal && int64_t(k0) + kBN - 1 > int64_t(q0w) + off) || (k0 + kBN > Lk);
+      if (edge) {
+        const int lim = row_lim - k0 - 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
+      mx = pair_max_halves(mx);
+      const float mt = mx * c_log2;
+      const bool move = mt > m_ref;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;
+        if (move) m_ref = mt;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      }
+      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
+          const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
+          l_run += p0 + p1;
+          pk[mb][r >> 1] = cvt_pk_bf16(p0, p1);
+        }
+    };
+
+    __syncthreads();  // the previous item's readers of every buffer are done
+    // Prologue: K(t0) into K buffer 0; stage K(t1) and V(t0).
+    bool m_cur = false, m_nxt = false;
+    int t_cur = walk.next(0, &m_cur);
+    int t_nxt = t_cur < kt_end ? walk.next(t_cur + 1, &m_nxt) : kt_end;
+    if (t_cur < kt_end) {
+      load_k(t_cur);
+      store_k(0);
+      load_v(t_cur);
+      if (t_nxt < kt_end) load_k(t_nxt);
+      pin_memory_order();
+    }
+    __syncthreads();
+
+    // n-th active tile: t_cur. prev: the tile whose V / P are pending (t_prev).
+    int t_prev = kt_end;  // none yet
+    bool vis_prev = false;
+    int n = 0;
+    while (true) {
+      const bool have_cur = t_cur < kt_end;
+      const bool have_prev = t_prev < kt_end;
+      if (!have_cur && !have_prev) break;
+      const bool vis_cur = have_cur && visible(t_cur, m_cur);
+      const int kb = n & 1, vb = (n - 1) & 1;
+      // ---- phase 2n ----
+      if (grpA) {
+        mblock(have_prev && vis_prev, vb, vis_cur, kb);
+      } else if (have_prev && vis_prev) {
+        vblock(t_prev);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- phase 2n+1 ----
+      if (grpA) {
+        if (vis_cur) vblock(t_cur);
+      } else {
+        mblock(have_prev && vis_prev, vb, vis_cur, kb);
+      }
+      // K(next) and V(cur) go to LDS; then the next loads are issued.
+      bool m_nn = false;
+      const int t_nn = t_nxt < kt_end ? walk.next(t_nxt + 1, &m_nn) : kt_end;
+      if (t_nxt < kt_end) store_k((n + 1) & 1);
+      if (have_cur) store_v(n & 1);
+      if (t_nxt < kt_end) load_v(t_nxt);
+      if (t_nn < kt_end) load_k(t_nn);
+      pin_memory_order();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      t_prev = t_cur;
+      vis_prev = vis_cur;
+      t_cur = t_nxt;
+      m_cur = m_nxt;
+      t_nxt = t_nn;
+      m_nxt = m_nn;
+      ++n;
+    }
+    // Group B's last softmax already ran in the final phase 2n (as vblock(t_prev)) and
+    // its last P.V in the final phase 2n+1; group A finished its P.V in the final phase 2n.
+
     const float l_tot = pair_sum_halves(l_run);
     const int qi = q0w + l32;
     if (qi < Lq) {
@@ -377,14 +730,49 @@ hipError_t launch_kernel(const void* q, const void* k, const void* v, void* o, f
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                     int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  constexpr int BM = 256;
+  const int n_qt = (Lq + BM - 1) / BM;
+  const int64_t n_items = int64_t(B) * H * n_qt;
+  int q_mode = 0;
+  float c = float(double(scale) * 1.4426950408889634);
+  if (scale < 0.f) {
+    q_mode = 1;
+    c = -c;
+  } else if (scale == 0.f) {
+    q_mode = 2;
+    c = 1.f;
+  }
+  const int64_t cap = 1LL << 22;
+  const unsigned grid = unsigned(n_items < cap ? n_items : cap);
+  const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
+  const size_t shmem = Smem<D>::BYTES;
+  static const hipError_t attr_err = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&attention_bf16_pp_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      int(shmem));
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL((attention_bf16_pp_kernel<D>), dim3(grid), dim3(512), shmem, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
+                     block_mask, n_qt, n_items, xcd_remap);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
                                  hipStream_t stream) {
-  if (d == 128)
+  if (d == 128) {
+#if RF_ATT_PINGPONG_D128
+    return launch_pp<128>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
+#else
     return launch_kernel<128, RF_ATT_NW_D128, RF_ATT_WPE_D128>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
                                                                 block_mask, stream);
+#endif
+  }
   return launch_kernel<64, RF_ATT_NW_D64, RF_ATT_WPE_D64>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask,
                                                            stream);
 }
