@@ -20,12 +20,17 @@
 //     accumulator rounded to bf16 (no data movement), because the order of
 //     keys inside an MFMA K-step is free as long as A and B agree; V^T is
 //     written to LDS transposed and key-permuted to match that order.
-//   - K and V^T tiles of BN = 64 keys are double-buffered in LDS: the global
-//     loads of tile n+1 are issued before the MFMAs of tile n, one barrier
-//     per tile.
-//   - Tiles above the causal diagonal or outside the block mask are never
-//     loaded or computed; the element mask is applied only on tiles that
-//     straddle the diagonal or the end of the keys.
+//   - K and V tiles of BN = 64 keys go straight from HBM into double-buffered
+//     LDS (buffer loads with an LDS destination), one barrier per tile.
+//   - The default kernel runs each wave's stages one tile apart: the score
+//     product of tile j+1 is issued between the exponentials of tile j, and
+//     the P.V product of tile j between the row maxima of tile j+1, so the
+//     matrix core and the vector ALU work side by side (K is therefore loaded
+//     two tiles ahead, V one).
+//   - Tiles above the causal diagonal or outside the block mask of the whole
+//     workgroup are never loaded or computed; the element mask is applied
+//     only on tiles that straddle the diagonal or the end of the keys, or
+//     that one wave's mask row hides while another's needs them.
 //   - Work items (b, h, query tile) are laid out so that all query tiles of
 //     a head run back to back on one XCD (its L2 serves the head's K/V to
 //     every tile), heaviest causal tiles first.
@@ -46,6 +51,30 @@ namespace {
 #endif
 #ifndef RF_ATT_NW_D64
 #define RF_ATT_NW_D64 2
+#endif
+#ifndef RF_ATT_DMA
+#define RF_ATT_DMA 1
+#endif
+#ifndef RF_ATT_SREAD_AHEAD
+#define RF_ATT_SREAD_AHEAD 4
+#endif
+#ifndef RF_ATT_VREAD_AHEAD
+#define RF_ATT_VREAD_AHEAD 2
+#endif
+#ifndef RF_ATT_SP
+#define RF_ATT_SP 1
+#endif
+#ifndef RF_ATT_SP_SCHED
+#define RF_ATT_SP_SCHED 1
+#endif
+#ifndef RF_ATT_SP_VALU_B
+#define RF_ATT_SP_VALU_B 2
+#endif
+#ifndef RF_ATT_BN_D128
+#define RF_ATT_BN_D128 64
+#endif
+#ifndef RF_ATT_BN_D64
+#define RF_ATT_BN_D64 64
 #endif
 #ifndef RF_ATT_PINGPONG_D128
 #define RF_ATT_PINGPONG_D128 0
@@ -106,8 +135,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 // lane i receives element i % 4 of the 8-byte rows supplied by lanes i/4,
 // i/4 + 4, i/4 + 8, i/4 + 12 of its group.
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(reinterpret_cast<uintptr_t>(p)));
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
   return __builtin_bit_cast(uint2, v);
 }
 
@@ -136,6 +164,7 @@ __device__ __forceinline__ void pin_memory_order() { asm volatile("" ::: "memory
 struct TileWalker {
   const uint8_t* mask;
   int n_mask_cols, mr0, mr1, mr_w, kt_end;
+  int bn;  // keys per tile (divides the 64-key mask tile)
   int base = -64;
   uint64_t wg_bits = 0, wv_bits = 0;
 
@@ -143,7 +172,7 @@ struct TileWalker {
     const int kt = b + int(threadIdx.x & 63);
     bool any = false, mine = false;
     if (kt < kt_end) {
-      const int mc = kt * kBN / kMaskTile;
+      const int mc = kt * bn / kMaskTile;
       for (int mr = mr0; mr <= mr1; ++mr) {
         const bool a = mask[int64_t(mr) * n_mask_cols + mc] != 0;
         any |= a;
@@ -236,7 +265,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     if (last_key > Lk - 1) last_key = Lk - 1;
     const int kt_end = last_key < 0 ? 0 : int(last_key / kBN) + 1;
     TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
-                    min(q0w, Lq - 1) / kMaskTile, kt_end};
+                    min(q0w, Lq - 1) / kMaskTile, kt_end, kBN};
 
     // Q^T fragments (B operand of S^T): lane holds row q0w + l32, d = 16 ks + 8 h .. + 8.
     uint4 qf[KSTEPS];
@@ -414,6 +443,680 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 }
 
 // ---------------------------------------------------------------------------
+// Direct-to-LDS variant. K and V tiles travel global -> LDS with buffer loads
+// that write LDS themselves (no staging registers, no LDS store instructions).
+// Such a load writes lane i's 16 bytes at (LDS base + 16 i), so a tile lands as
+// unpadded rows; bank conflicts are avoided by XOR-swizzling the 16-byte chunks
+// of each row instead: K chunk c of row r sits in slot c ^ (r mod KCH), which
+// spreads the 16 rows that one 16-lane read touches over 16 slots; V chunk c of
+// row r sits in slot c ^ s(r mod 4) (s = 4 for d = 128, 2 for d = 64), which
+// spreads the 4 rows x 2 chunks of one transposed 16-lane read over 8 slots.
+// The sweep is unrolled by two so the buffer being read and the buffer being
+// filled are distinct LDS objects at compile time: reads never wait for the
+// other buffer's loads, and the end-of-tile barrier (which waits for this
+// wave's loads) publishes the next tile.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Swz {
+  static constexpr int KCH = D / 8;
+  static constexpr int VX = D >= 128 ? 4 : 2;
+  __device__ static int k_slot(int row, int c) { return c ^ (row & (KCH - 1)); }
+  __device__ static int v_slot(int row, int c) { return c ^ (VX * (row & 3)); }
+};
+
+// Issue one tile's worth of direct-to-LDS loads for K and V: this wave's n
+// instructions, each writing 64 x 16 contiguous bytes of LDS. Device-only (the
+// LDS address-space cast has no host meaning).
+__device__ __forceinline__ void dma_tile(const uint16_t* khead, const uint16_t* vhead, uint32_t head_bytes,
+                                         uint16_t* kdst, uint16_t* vdst, uint32_t base, const uint32_t* kv_off,
+                                         const uint32_t* vv_off, int ins0, int n) {
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(khead, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vhead, head_bytes);
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const int ins = ins0 + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (__attribute__((address_space(3))) void*)(kdst + ins * 512), 16,
+                                             base + kv_off[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vdst + ins * 512), 16,
+                                             base + vv_off[j], 0, 0, 0);
+  }
+}
+
+// One tensor's share of a tile: this wave's n direct-to-LDS instructions.
+__device__ __forceinline__ void dma_one(const uint16_t* head, uint32_t head_bytes, uint16_t* dst, uint32_t base,
+                                        const uint32_t* lane_off, int ins0, int n) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, head_bytes);
+#pragma unroll
+  for (int j = 0; j < n; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (ins0 + j) * 512), 16,
+                                             base + lane_off[j], 0, 0, 0);
+}
+
+template <int D, int NW, int WPE, int BN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_dma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
+    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap) {
+  constexpr int NT = NW * 64;
+  constexpr int BM = 32 * NW;
+  constexpr int KCH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int MB = BN / 32;                 // 32-key blocks per tile
+  constexpr int PVK = BN / 16;                // MFMA K-steps of the P.V product per tile
+  constexpr int CHUNKS = BN * KCH;            // 16-byte chunks per K (or V) tile
+  constexpr int INSTR = CHUNKS / 64;          // wave-wide DMA instructions per tile and tensor
+  constexpr int IPW = INSTR / NW;             // ... per wave
+  static_assert(INSTR % NW == 0, "tile split");
+  static_assert(BN % 32 == 0 && BN <= kMaskTile, "tile size");
+  using SW = Swz<D>;
+
+  __shared__ __align__(16) uint16_t kb0[BN * D];
+  __shared__ __align__(16) uint16_t kb1[BN * D];
+  __shared__ __align__(16) uint16_t vb0[BN * D];
+  __shared__ __align__(16) uint16_t vb1[BN * D];
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int64_t off = int64_t(Lk) - Lq;
+  const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
+  const int64_t per_xcd = n_items / 8;
+  const uint32_t head_bytes = uint32_t(Lk) * D * 2;
+
+  // This lane's source chunk for each of its DMA instructions (same for K and V
+  // up to the swizzle), relative to the tile start.
+  uint32_t kv_off[IPW], vv_off[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int g = 64 * (wave * IPW + j) + lane;
+    const int row = g / KCH, slot = g % KCH;
+    // slot = swizzle(row, c) is an involution in c: c = swizzle(row, slot)
+    kv_off[j] = uint32_t(row * D * 2 + 16 * SW::k_slot(row, slot));
+    vv_off[j] = uint32_t(row * D * 2 + 16 * SW::v_slot(row, slot));
+  }
+  // Transposed V^T read addressing (see lds_read_tr16).
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_x = (lane >> 4) & 1, tr_y = lane & 3;
+
+  for (int64_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
+    const int64_t item = xcd_remap ? (gi % 8) * per_xcd + gi / 8 : gi;
+    const int64_t bh = item / n_qt;
+    const int qr = int(item % n_qt);
+    const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
+    const int q0w = q0 + 32 * wave;
+    const uint16_t* qh = q + bh * int64_t(Lq) * D;
+    const uint16_t* khead = k + bh * int64_t(Lk) * D;
+    const uint16_t* vhead = v + bh * int64_t(Lk) * D;
+
+    int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
+    if (last_key > Lk - 1) last_key = Lk - 1;
+    const int kt_end = last_key < 0 ? 0 : int(last_key / BN) + 1;
+    // The walker works on 64-key mask columns; tiles of BN keys map to column kt * BN / 64.
+    TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+                    min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
+
+    uint4 qf[KSTEPS];
+    {
+      const int qi = q0w + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (qi < Lq) x = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * ks + 8 * h);
+        if (q_mode == 1) { x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u; }
+        if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
+        qf[ks] = x;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    f32x16_t acc_o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+    float m_ref = kNegInf, l_run = 0.f, l_rnd = 0.f;
+    const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
+    const int row_lim = int(row_last < int64_t(Lk) - 1 ? (row_last < -1 ? -1 : row_last) : int64_t(Lk) - 1);
+
+
+    auto compute = [&](const uint16_t* ks_, const uint16_t* vs_, int kt, bool mine) {
+      const int k0 = kt * BN;
+      const bool wave_visible = (!causal || int64_t(k0) <= int64_t(q0w) + 31 + off) && q0w < Lq && mine;
+      if (!wave_visible) return;
+      // Score MFMAs: the 32-key blocks (and, with one block, the even / odd K-steps)
+      // accumulate in separate registers so consecutive MFMAs never depend on
+      // each other.
+      constexpr int NACC = MB >= 2 ? MB : 2;
+      f32x16_t st[MB];
+      f32x16_t sacc[NACC];
+#pragma unroll
+      for (int a = 0; a < NACC; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[a][r] = 0.f;
+      // All K fragments are read first and the MFMAs follow with a fixed read-ahead
+      // (RF_ATT_SREAD_AHEAD reads in flight): LDS latency is several MFMA issue
+      // slots, so a one-deep read / multiply alternation would stall every step.
+      uint4 kfrag[KSTEPS * MB];
+#pragma unroll
+      for (int kstep = 0; kstep < KSTEPS; ++kstep)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = 32 * mb + l32;
+          kfrag[kstep * MB + mb] =
+              *reinterpret_cast<const uint4*>(ks_ + row * D + 8 * SW::k_slot(row, 2 * kstep + h));
+        }
+#pragma unroll
+      for (int kstep = 0; kstep < KSTEPS; ++kstep)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int acc = MB >= 2 ? mb : (kstep & 1);
+          sacc[acc] = mfma32(as_bf16x8(kfrag[kstep * MB + mb]), as_bf16x8(qf[kstep]), sacc[acc]);
+        }
+#if RF_ATT_SREAD_AHEAD > 0
+      __builtin_amdgcn_sched_group_barrier(0x100, RF_ATT_SREAD_AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < KSTEPS * MB - RF_ATT_SREAD_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, RF_ATT_SREAD_AHEAD, 0);
+#endif
+      if constexpr (MB >= 2) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) st[mb] = sacc[mb];
+      } else {
+        st[0] = sacc[0] + sacc[1];
+      }
+      const bool edge = (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
+      if (edge) {
+        const int lim = row_lim - k0 - 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
+      mx = pair_max_halves(mx);
+      const float mt = mx * c_log2;
+      const bool move = mt > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float alpha = move ? fast_exp2(m_ref - mt) : 1.f;
+        if (move) m_ref = mt;
+        l_run *= alpha;
+        l_rnd *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+      }
+      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+      uint32_t pk[MB][8];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
+          const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
+          const uint32_t pp = cvt_pk_bf16(p0, p1);
+          l_run += p0 + p1;
+          l_rnd = add_bf16_pair(pp, l_rnd);
+          pk[mb][r >> 1] = pp;
+        }
+      // V^T fragments for the P.V products, product i = kstep * DB + db, read in a
+      // rolling window of VAHEAD fragments ahead of the product that uses them.
+      constexpr int NPV = PVK * DB;
+      constexpr int VAHEAD = RF_ATT_VREAD_AHEAD > 0 ? RF_ATT_VREAD_AHEAD : 1;
+      auto vread = [&](int i) {
+        const int kstep = i / DB, db = i % DB;
+        const int row_lo = 16 * kstep + tr_row, row_hi = row_lo + 8;
+        const int c = 4 * db + 2 * tr_x + (tr_y >> 1);
+        const uint2 lo = lds_read_tr16(vs_ + row_lo * D + 8 * SW::v_slot(row_lo, c) + 4 * (tr_y & 1));
+        const uint2 hi = lds_read_tr16(vs_ + row_hi * D + 8 * SW::v_slot(row_hi, c) + 4 * (tr_y & 1));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 vfrag[VAHEAD];
+#pragma unroll
+      for (int i = 0; i < VAHEAD; ++i) vfrag[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kstep = i / DB, db = i % DB;
+        const int mb = kstep >> 1, r0 = (kstep & 1) * 4;
+        const uint4 bp = make_uint4(pk[mb][r0], pk[mb][r0 + 1], pk[mb][r0 + 2], pk[mb][r0 + 3]);
+        const uint4 a = vfrag[i % VAHEAD];
+        if (i + VAHEAD < NPV) vfrag[i % VAHEAD] = vread(i + VAHEAD);
+        acc_o[db] = mfma32(as_bf16x8(a), as_bf16x8(bp), acc_o[db]);
+      }
+#if RF_ATT_VREAD_AHEAD > 0
+      // Same read-ahead for the two transposed V reads behind each P.V product.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * RF_ATT_VREAD_AHEAD, 1);
+#pragma unroll
+      for (int i = 0; i < PVK * DB - RF_ATT_VREAD_AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, RF_ATT_VREAD_AHEAD, 1);
+#endif
+    };
+
+    __syncthreads();  // the previous item's readers of every buffer are done
+    bool mine = false;
+    int kt = walk.next(0, &mine);
+    if (kt < kt_end) dma_tile(khead, vhead, head_bytes, kb0, vb0, uint32_t(kt) * BN * D * 2, kv_off, vv_off, wave * IPW, IPW);
+    __syncthreads();  // waits for this wave's loads, then publishes tile 0
+    while (kt < kt_end) {
+      // even step: read buffers 0, fill buffers 1
+      bool mine1 = false;
+      const int kt1 = walk.next(kt + 1, &mine1);
+      if (kt1 < kt_end) dma_tile(khead, vhead, head_bytes, kb1, vb1, uint32_t(kt1) * BN * D * 2, kv_off, vv_off, wave * IPW, IPW);
+      compute(kb0, vb0, kt, mine);
+      __syncthreads();
+      if (kt1 >= kt_end) break;
+      // odd step: read buffers 1, fill buffers 0
+      bool mine2 = false;
+      const int kt2 = walk.next(kt1 + 1, &mine2);
+      if (kt2 < kt_end) dma_tile(khead, vhead, head_bytes, kb0, vb0, uint32_t(kt2) * BN * D * 2, kv_off, vv_off, wave * IPW, IPW);
+      compute(kb1, vb1, kt1, mine1);
+      __syncthreads();
+      kt = kt2;
+      mine = mine2;
+    }
+
+    const float l_tot = pair_sum_halves(l_run);
+    const float l_rtot = pair_sum_halves(l_rnd);
+    const int qi = q0w + l32;
+    if (qi < Lq) {
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_rtot : 0.f;
+      uint16_t* orow = o + (bh * Lq + qi) * int64_t(D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * db + 8 * r4 + 4 * h;
+          uint2 pkt;
+          pkt.x = cvt_pk_bf16(acc_o[db][4 * r4] * inv, acc_o[db][4 * r4 + 1] * inv);
+          pkt.y = cvt_pk_bf16(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = pkt;
+        }
+      if (lse != nullptr && h == 0) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined variant of the direct-to-LDS kernel.
+//
+// Within one wave the three stages of a key tile (score product, softmax
+// update, P.V product) depend on each other, so run back to back they leave
+// the matrix core idle during the exponentials and the vector ALU idle during
+// the products. Here every wave runs them one tile apart:
+//
+//   phase A of tile j :  S(j+1) = K(j+1) Q^T      while  P(j) = exp(S(j) - m)
+//   phase B of tile j :  O^T   += V(j)^T P(j)^T   while  m <- max(m, rowmax S(j+1))
+//
+// so each phase pairs a run of MFMAs with independent vector work. The score
+// product of the next tile needs its K one tile earlier than its V, so K is
+// loaded two tiles ahead and V one tile ahead; both stay double-buffered and
+// one barrier per tile both publishes the loads and frees the buffers:
+//
+//   after the barrier of tile j:  load K(j+2) -> the K buffer of tile j,
+//                                 load V(j+1) -> the V buffer of tile j-1.
+//
+// The softmax state follows the same lazy rescale as the other kernels: the
+// running reference m only moves (and O and the sums are only rescaled) when
+// a tile's row maximum exceeds it by more than 2^kRescaleSlack. The rescale
+// of O waits for the P.V product that precedes it in phase B.
+// ---------------------------------------------------------------------------
+template <int D, int NW, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
+    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap) {
+  constexpr int BN = 64;
+  constexpr int BM = 32 * NW;
+  constexpr int KCH = D / 8;
+  constexpr int KSTEPS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int MB = BN / 32;
+  constexpr int PVK = BN / 16;
+  constexpr int NS = KSTEPS * MB;   // score MFMAs per tile
+  constexpr int NPV = PVK * DB;     // P.V MFMAs per tile
+  constexpr int CHUNKS = BN * KCH;
+  constexpr int INSTR = CHUNKS / 64;
+  constexpr int IPW = INSTR / NW;
+  static_assert(INSTR % NW == 0, "tile split");
+  using SW = Swz<D>;
+
+  __shared__ __align__(16) uint16_t kb0[BN * D];
+  __shared__ __align__(16) uint16_t kb1[BN * D];
+  __shared__ __align__(16) uint16_t vb0[BN * D];
+  __shared__ __align__(16) uint16_t vb1[BN * D];
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int64_t off = int64_t(Lk) - Lq;
+  const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
+  const int64_t per_xcd = n_items / 8;
+  const uint32_t head_bytes = uint32_t(Lk) * D * 2;
+
+  uint32_t kv_off[IPW], vv_off[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int g = 64 * (wave * IPW + j) + lane;
+    const int row = g / KCH, slot = g % KCH;
+    kv_off[j] = uint32_t(row * D * 2 + 16 * SW::k_slot(row, slot));
+    vv_off[j] = uint32_t(row * D * 2 + 16 * SW::v_slot(row, slot));
+  }
+  const int tr_row = 4 * h + ((lane & 15) >> 2);
+  const int tr_x = (lane >> 4) & 1, tr_y = lane & 3;
+
+  for (int64_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
+    const int64_t item = xcd_remap ? (gi % 8) * per_xcd + gi / 8 : gi;
+    const int64_t bh = item / n_qt;
+    const int qr = int(item % n_qt);
+    const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
+    const int q0w = q0 + 32 * wave;
+    const uint16_t* qh = q + bh * int64_t(Lq) * D;
+    const uint16_t* khead = k + bh * int64_t(Lk) * D;
+    const uint16_t* vhead = v + bh * int64_t(Lk) * D;
+
+    int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
+    if (last_key > Lk - 1) last_key = Lk - 1;
+    const int kt_end = last_key < 0 ? 0 : int(last_key / BN) + 1;
+    TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+                    min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
+
+    uint4 qf[KSTEPS];
+    {
+      const int qi = q0w + l32;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (qi < Lq) x = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * ks + 8 * h);
+        if (q_mode == 1) { x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u; }
+        if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
+        qf[ks] = x;
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+
+    f32x16_t acc_o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+    float m_ref = kNegInf, l_run = 0.f, l_rnd = 0.f;
+    const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
+    const int row_lim = int(row_last < int64_t(Lk) - 1 ? (row_last < -1 ? -1 : row_last) : int64_t(Lk) - 1);
+
+    // ---- stage pieces (inlined into the phase bodies below) ----
+    auto score_mfmas = [&](const uint16_t* ks_, f32x16_t (&sacc)[MB]) {
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[a][r] = 0.f;
+      // K fragments in a rolling window of KAHEAD reads ahead of their product.
+      constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
+      auto kread = [&](int i) {
+        const int kstep = i / MB, mb = i % MB;
+        const int row = 32 * mb + l32;
+        return *reinterpret_cast<const uint4*>(ks_ + row * D + 8 * SW::k_slot(row, 2 * kstep + h));
+      };
+      uint4 kfrag[KAHEAD];
+#pragma unroll
+      for (int i = 0; i < KAHEAD; ++i) kfrag[i] = kread(i);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int kstep = i / MB, mb = i % MB;
+        const uint4 a = kfrag[i % KAHEAD];
+        if (i + KAHEAD < NS) kfrag[i % KAHEAD] = kread(i + KAHEAD);
+        sacc[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[kstep]), sacc[mb]);
+      }
+    };
+    auto exp_tile = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8]) {
+      const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
+          const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
+          const uint32_t pp = cvt_pk_bf16(p0, p1);
+          l_run += p0 + p1;
+          l_rnd = add_bf16_pair(pp, l_rnd);
+          pk[mb][r >> 1] = pp;
+        }
+    };
+    auto pv_mfmas = [&](const uint16_t* vs_, const uint32_t (&pk)[MB][8]) {
+      constexpr int VAHEAD = RF_ATT_VREAD_AHEAD > 0 ? RF_ATT_VREAD_AHEAD : 1;
+      auto vread = [&](int i) {
+        const int kstep = i / DB, db = i % DB;
+        const int row_lo = 16 * kstep + tr_row, row_hi = row_lo + 8;
+        const int c = 4 * db + 2 * tr_x + (tr_y >> 1);
+        const uint2 lo = lds_read_tr16(vs_ + row_lo * D + 8 * SW::v_slot(row_lo, c) + 4 * (tr_y & 1));
+        const uint2 hi = lds_read_tr16(vs_ + row_hi * D + 8 * SW::v_slot(row_hi, c) + 4 * (tr_y & 1));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+      };
+      uint4 vfrag[VAHEAD];
+#pragma unroll
+      for (int i = 0; i < VAHEAD; ++i) vfrag[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int kstep = i / DB, db = i % DB;
+        const int mb = kstep >> 1, r0 = (kstep & 1) * 4;
+        const uint4 bp = make_uint4(pk[mb][r0], pk[mb][r0 + 1], pk[mb][r0 + 2], pk[mb][r0 + 3]);
+        const uint4 a = vfrag[i % VAHEAD];
+        if (i + VAHEAD < NPV) vfrag[i % VAHEAD] = vread(i + VAHEAD);
+        acc_o[db] = mfma32(as_bf16x8(a), as_bf16x8(bp), acc_o[db]);
+      }
+    };
+    // Scores this wave must not see -> -inf: keys past the row's last key (causal
+    // diagonal, sequence end), and the whole tile when the wave's block-mask row
+    // skips it or the causal diagonal ends before it. A fully hidden tile then
+    // contributes exp(-inf) = 0 everywhere.
+    auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine) {
+      const int k0 = kt * BN;
+      const bool edge = !mine || (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
+      if (edge) {
+        const int lim = mine ? row_lim - k0 - 4 * h : -BN;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
+      }
+    };
+    // Row maximum of a tile; moves the reference when it is exceeded by more than
+    // the slack and returns the factor for the state accumulated so far.
+    auto tile_max = [&](const f32x16_t (&st)[MB], bool* moved) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
+      mx = pair_max_halves(mx);
+      const float mt = mx * c_log2;
+      const bool move = mt > m_ref + kRescaleSlack;
+      *moved = __builtin_amdgcn_ballot_w64(move) != 0;
+      float alpha = 1.f;
+      if (move) {
+        alpha = fast_exp2(m_ref - mt);
+        m_ref = mt;
+      }
+      return alpha;
+    };
+    auto rescale = [&](float alpha) {
+      l_run *= alpha;
+      l_rnd *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+    };
+
+    // One steady-state step: current tile (scores s_cur, V in vs_cur), next tile
+    // (K in ks_next, scores into s_next).
+    auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
+                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next) {
+      uint32_t pk[MB][8];
+      // Phase A: score product of the next tile with the exponentials of this
+      // one, written as NS chunks of one MFMA plus its share of the vector work
+      // (fenced so the compiler keeps the interleave).
+      {
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_next[a][r] = 0.f;
+        constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
+        constexpr int PAIRS = MB * 8;             // score pairs per lane and tile
+        constexpr int PPC = (PAIRS + NS - 1) / NS;  // pairs per chunk
+        auto kread = [&](int i) {
+          const int kstep = i / MB, mb = i % MB;
+          const int row = 32 * mb + l32;
+          return *reinterpret_cast<const uint4*>(ks_next + row * D + 8 * SW::k_slot(row, 2 * kstep + h));
+        };
+        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+        uint4 kfrag[KAHEAD];
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) kfrag[i] = kread(i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const int kstep = i / MB, mb = i % MB;
+          const uint4 a = kfrag[i % KAHEAD];
+          if (i + KAHEAD < NS) kfrag[i % KAHEAD] = kread(i + KAHEAD);
+          s_next[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[kstep]), s_next[mb]);
+#pragma unroll
+          for (int j = 0; j < PPC; ++j) {
+            const int pr = i * PPC + j;
+            if (pr < PAIRS) {
+              const int cb = pr / 8, r = 2 * (pr % 8);
+              const float p0 = fast_exp2(fmaf(s_cur[cb][r], c_log2, -mu));
+              const float p1 = fast_exp2(fmaf(s_cur[cb][r + 1], c_log2, -mu));
+              const uint32_t pp = cvt_pk_bf16(p0, p1);
+              l_run += p0 + p1;
+              l_rnd = add_bf16_pair(pp, l_rnd);
+              pk[cb][r >> 1] = pp;
+            }
+          }
+#if RF_ATT_SP_SCHED
+          __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+      }
+      // Keep P and the sums in phase A: without these uses the compiler sinks
+      // the exponentials past the mask branch, next to the P.V product.
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[mb][i]));
+      asm volatile("" ::"v"(l_run), "v"(l_rnd));
+      mask_tile(s_next, kt_next, mine_next);
+      // Phase B: P.V product of this tile with the row maximum of the next one.
+      pv_mfmas(vs_cur, pk);
+      bool moved = false;
+      const float alpha = tile_max(s_next, &moved);
+#if RF_ATT_SP_SCHED
+      {
+        constexpr int VAHEAD = RF_ATT_VREAD_AHEAD > 0 ? RF_ATT_VREAD_AHEAD : 1;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VAHEAD, 1);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+          if (i < NPV - VAHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+          __builtin_amdgcn_sched_group_barrier(0x002, RF_ATT_SP_VALU_B, 1);
+        }
+      }
+#endif
+      if (moved) rescale(alpha);
+    };
+    // The last tile: exponentials and P.V product only.
+    auto finish = [&](const uint16_t* vs_cur, const f32x16_t (&s_cur)[MB]) {
+      uint32_t pk[MB][8];
+      exp_tile(s_cur, pk);
+      pv_mfmas(vs_cur, pk);
+    };
+    f32x16_t s0[MB], s1[MB];
+
+    __syncthreads();  // the previous item's readers of every buffer are done
+    bool m0 = false, m1 = false, m2 = false;
+    int t0 = walk.next(0, &m0);
+    if (t0 < kt_end) {
+      int t1 = walk.next(t0 + 1, &m1);
+      dma_one(khead, head_bytes, kb0, uint32_t(t0) * BN * D * 2, kv_off, wave * IPW, IPW);
+      dma_one(vhead, head_bytes, vb0, uint32_t(t0) * BN * D * 2, vv_off, wave * IPW, IPW);
+      if (t1 < kt_end) dma_one(khead, head_bytes, kb1, uint32_t(t1) * BN * D * 2, kv_off, wave * IPW, IPW);
+      __syncthreads();  // K(t0), K(t1), V(t0) resident
+      score_mfmas(kb0, s0);
+      mask_tile(s0, t0, m0);
+      {
+        bool moved = false;
+        const float alpha = tile_max(s0, &moved);
+        if (moved) rescale(alpha);
+      }
+      // Steady state, unrolled by two: in the even step the current tile's V is
+      // in vb0 and the next tile's K in kb1; the odd step mirrors it. The loop
+      // leaves with the last tile's scores in s0 and its V in vb0 or vb1.
+      bool last_in_vb1 = false;
+      while (true) {
+        __syncthreads();  // loads of the previous step resident; kb0 and vb1 free
+        if (t1 >= kt_end) break;
+        int t2 = walk.next(t1 + 1, &m2);
+        if (t2 < kt_end) dma_one(khead, head_bytes, kb0, uint32_t(t2) * BN * D * 2, kv_off, wave * IPW, IPW);
+        dma_one(vhead, head_bytes, vb1, uint32_t(t1) * BN * D * 2, vv_off, wave * IPW, IPW);
+        step(kb1, vb0, s0, s1, t1, m1);
+
+        __syncthreads();  // kb1 and vb0 free
+        if (t2 >= kt_end) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) s0[mb] = s1[mb];
+          last_in_vb1 = true;
+          break;
+        }
+        bool m3 = false;
+        const int t3 = walk.next(t2 + 1, &m3);
+        if (t3 < kt_end) dma_one(khead, head_bytes, kb1, uint32_t(t3) * BN * D * 2, kv_off, wave * IPW, IPW);
+        dma_one(vhead, head_bytes, vb0, uint32_t(t2) * BN * D * 2, vv_off, wave * IPW, IPW);
+        step(kb0, vb1, s1, s0, t2, m2);
+        t1 = t3;
+        m1 = m3;
+      }
+      finish(last_in_vb1 ? vb1 : vb0, s0);
+    }
+
+    const float l_tot = pair_sum_halves(l_run);
+    const float l_rtot = pair_sum_halves(l_rnd);
+    const int qi = q0w + l32;
+    if (qi < Lq) {
+      const bool live = l_tot > 0.f;
+      const float inv = live ? 1.f / l_rtot : 0.f;
+      uint16_t* orow = o + (bh * Lq + qi) * int64_t(D);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * db + 8 * r4 + 4 * h;
+          uint2 pkt;
+          pkt.x = cvt_pk_bf16(acc_o[db][4 * r4] * inv, acc_o[db][4 * r4 + 1] * inv);
+          pkt.y = cvt_pk_bf16(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d0) = pkt;
+        }
+      if (lse != nullptr && h == 0) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Ping-pong variant for long causal / dense sweeps (d = 128).
 //
 // Eight waves form two groups of four; each SIMD holds one wave of each group.
@@ -490,7 +1193,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (last_key > Lk - 1) last_key = Lk - 1;
     const int kt_end = last_key < 0 ? 0 : int(last_key / kBN) + 1;
     TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
-                    min(q0w, Lq - 1) / kMaskTile, kt_end};
+                    min(q0w, Lq - 1) / kMaskTile, kt_end, kBN};
     auto visible = [&](int kt, bool mine) {
       return (!causal || int64_t(kt) * kBN <= int64_t(q0w) + 31 + off) && q0w < Lq && mine;
     };
@@ -760,11 +1463,49 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
   return hipGetLastError();
 }
 
+template <int D, int NW, int WPE, int BN, bool SP>
+hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                      int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  const int n_qt = (Lq + BM - 1) / BM;
+  const int64_t n_items = int64_t(B) * H * n_qt;
+  int q_mode = 0;
+  float c = float(double(scale) * 1.4426950408889634);
+  if (scale < 0.f) {
+    q_mode = 1;
+    c = -c;
+  } else if (scale == 0.f) {
+    q_mode = 2;
+    c = 1.f;
+  }
+  const int64_t cap = 1LL << 22;
+  const unsigned grid = unsigned(n_items < cap ? n_items : cap);
+  const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
+  if constexpr (SP)
+    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE>), dim3(grid), dim3(NW * 64), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
+                       block_mask, n_qt, n_items, xcd_remap);
+  else
+    hipLaunchKernelGGL((attention_bf16_dma_kernel<D, NW, WPE, BN>), dim3(grid), dim3(NW * 64), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
+                       block_mask, n_qt, n_items, xcd_remap);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
                                  hipStream_t stream) {
+#if RF_ATT_DMA
+  if (d == 128)
+    return launch_dma<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, RF_ATT_SP ? 64 : RF_ATT_BN_D128, bool(RF_ATT_SP)>(
+        q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
+  return launch_dma<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, RF_ATT_SP ? 64 : RF_ATT_BN_D64, bool(RF_ATT_SP)>(
+      q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
+#endif
   if (d == 128) {
 #if RF_ATT_PINGPONG_D128
     return launch_pp<128>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask, stream);
