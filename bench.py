@@ -37,7 +37,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 KERNEL_SOURCES = {
-    "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
+    "copy": None, "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip",
 }
 
@@ -59,7 +59,7 @@ def measured_traffic(workload: str):
         t = json.load(open(p)).get(workload)
     except (OSError, ValueError):
         return None
-    if not t or t.get("source_sha") != source_sha(KERNEL_SOURCES[workload]):
+    if not t or KERNEL_SOURCES.get(workload) is None or t.get("source_sha") != source_sha(KERNEL_SOURCES[workload]):
         return None
     return t.get("bytes_per_launch")
 
@@ -178,31 +178,47 @@ def setup_attn_f32(rf, torch, W):
                 unit="TFLOP/s", bound="alu", keep=(q, k, v, o, lse), cfg=c)
 
 
-SETUPS = {"softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
+def setup_copy(rf, torch, W):
+    """Counter calibration only (not run by default): a plain torch elementwise
+    copy of 1 GiB fp32, whose HBM traffic is known (one read, one write)."""
+    n = 1 << 28
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    return dict(fn=lambda: torch.mul(x, 1.0, out=y), work=2 * n * 4, unit="GB/s", bound="hbm", keep=(x, y),
+                cfg={"name": "calibration_copy_f32_1GiB", "dtype": "f32"})
+
+
+SETUPS = {"copy": setup_copy, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
           "attn_f32": setup_attn_f32}
-NAMES = {"softmax": 2, "prefill": 3, "decode": 4, "sparse": 5, "attn_f32": 1}
 
 
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample of the headline workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_softmax(W, budget_s=12.0):
+def cpu_baseline_softmax(W, budget_s=10.0):
+    """The fp64 oracle over the headline workload's rows, 64 rows at a time,
+    repeating whole passes until about budget_s of oracle time is spent."""
     import oracle
     c = W.CONFIGS[2]
+    chunk = 64
     rows = 0
     spent = 0.0
-    chunk = 64
-    while spent < budget_s and rows < c["rows"]:
-        x = W.softmax_rows_input(2, chunk, c["cols"], row_ids=range(rows, rows + chunk))
-        t0 = time.perf_counter()
+    cpu = 0.0
+    while spent < budget_s:
+        r0 = rows % c["rows"]
+        x = W.softmax_rows_input(2, chunk, c["cols"], row_ids=range(r0, r0 + chunk))
+        t0, p0 = time.perf_counter(), time.process_time()
         oracle.softmax_rows(x)
         spent += time.perf_counter() - t0
+        cpu += time.process_time() - p0
         rows += chunk
     gbs = 2 * rows * c["cols"] * 4 / spent / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {c['rows']} rows x {c['cols']} cols (fp64 NumPy three-pass softmax, "
-                      f"{spent:.1f} s, single-threaded)"}
+    cores = max(1, round(cpu / spent))   # threads the oracle kept busy (process CPU time / wall time)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} rows x {c['cols']} cols ({rows / c['rows']:.2f} passes over the {c['rows']} rows; "
+                      f"fp64 NumPy three-pass softmax, {spent:.1f} s of oracle time, "
+                      f"{cpu / spent:.2f} CPU-s per s)"}
 
 
 def main():
@@ -228,6 +244,7 @@ def main():
 
     wanted = [w.strip() for w in args.workloads.split(",") if w.strip()]
     results = {}
+    cfgs = {}
     timer = Timer(torch)
     for name in wanted:
         log(f"{name}: setup")
@@ -258,13 +275,14 @@ def main():
             r["partial_kernel_ms"] = round(kern_ms, 5)
         r.update(s.get("extra", {}))
         results[name] = r
+        cfgs[name] = s["cfg"]
         log(f"{name}: {r['value']} {r['unit']} ({call_ms:.4f} ms/call, frac {r['roofline']['frac']})")
         del s
         torch.cuda.empty_cache()
 
     head = "softmax" if "softmax" in results else wanted[0]
     h = results[head]
-    hc = W.CONFIGS[NAMES[head]]
+    hc = cfgs[head]
     out = {
         "metric": "fused attention TFLOP/s (% bf16 MFMA peak); softmax/decode GB/s (% HBM peak)",
         "value": h["value"], "unit": h["unit"], "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -1,0 +1,81 @@
+"""Host-side logic of the benchmark and the traffic converter (no GPU needed)."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from online_softmax_attention_pass_amd import traffic  # noqa: E402
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def _write_counters(path, counter, rows):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for i, (name, value) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_traffic_scales_by_the_copy_calibration(tmp_path):
+    copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<MulFunctor<float> > >(int)"
+    names = {
+        "softmax": "void rf::softmax_rows_reg<float, 4, 512, 16>(float const*)",
+        "prefill": "void rf::attention_bf16_sp_kernel<128, 4, 2>(unsigned short const*)",
+        "sparse": "void rf::attention_bf16_sp_kernel<64, 2, 2>(unsigned short const*)",
+        "decode": "void rf::decode_partial_kernel<128, 8>(unsigned short const*)",
+        "attn_f32": "void rf::attention_f32_kernel<64>(float const*)",
+    }
+    # the fetch counter reads half of the copy's 1 GiB, the write counter all of it
+    fetch = [(copy, 524288.0), (copy, 524288.0)] + [(n, 1000.0 * (i + 1)) for i, n in enumerate(names.values())]
+    fetch += [(names["prefill"], 3000.0)]                         # second dispatch: mean is 2500
+    write = [(copy, 1048576.0)] + [(n, 10.0 * (i + 1)) for i, n in enumerate(names.values())]
+    fcsv, wcsv, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
+    _write_counters(fcsv, "FETCH_SIZE", fetch)
+    _write_counters(wcsv, "WRITE_SIZE", write)
+    traffic.main([str(fcsv), str(wcsv), str(out)])
+    t = json.load(open(out))
+    assert t["calibration"]["fetch_bytes_per_kib"] == pytest.approx(2048.0)
+    assert t["calibration"]["write_bytes_per_kib"] == pytest.approx(1024.0)
+    assert t["softmax"]["fetch_bytes"] == 1000 * 2048
+    assert t["prefill"]["fetch_bytes"] == 2500 * 2048
+    assert t["prefill"]["write_bytes"] == 20 * 1024
+    assert t["decode"]["bytes_per_launch"] == 4000 * 2048 + 40 * 1024
+    assert t["prefill"]["source_sha"] == traffic.source_sha("attention_bf16.hip")
+
+
+def test_traffic_rejects_an_ambiguous_kernel(tmp_path):
+    copy = "vectorized_elementwise_kernel<MulFunctor>"
+    rows = [(copy, 1.0), ("softmax_rows_reg<float, 4>", 1.0), ("softmax_rows_stream<float>", 1.0)]
+    fcsv, wcsv = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_counters(fcsv, "FETCH_SIZE", rows)
+    _write_counters(wcsv, "WRITE_SIZE", rows)
+    with pytest.raises(SystemExit):
+        traffic.main([str(fcsv), str(wcsv), str(tmp_path / "t.json")])
+
+
+def test_bench_reports_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
+    import bench
+    os.makedirs(tmp_path / "profiles")
+    sha = bench.source_sha("softmax_rows.hip")
+    json.dump({"softmax": {"source_sha": sha, "bytes_per_launch": 123},
+               "decode": {"source_sha": "0" * 16, "bytes_per_launch": 456}},
+              open(tmp_path / "profiles" / "traffic.json", "w"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_sha", lambda name: sha if name == "softmax_rows.hip" else "f" * 16)
+    assert bench.measured_traffic("softmax") == 123
+    assert bench.measured_traffic("decode") is None      # kernel changed since the counters were taken
+    assert bench.measured_traffic("prefill") is None     # never measured
+    assert bench.measured_traffic("copy") is None        # calibration only
