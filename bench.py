@@ -14,6 +14,9 @@ active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds).
 Timing: inputs are resident in HBM before the timed region; W untimed
 warm-up calls; then K calls, each bracketed by HIP events recorded on the
 stream the kernels run on; the whole region is bracketed by device syncs.
+The softmax workload (HBM-bound, 1 GiB per call) alternates two buffer sets
+so that no call is served from the 256 MB Infinity Cache; decode's 32 GiB
+cannot be cached; the MFMA-bound attention workloads use one set.
 The CPU baseline times the fp64 oracle on a bounded sample of the headline
 workload, on this host's cores, and scales it to the same unit.
 """
@@ -100,13 +103,23 @@ def roofline(bound, achieved, peak, unit, traffic):
 # ---------------------------------------------------------------------------
 
 def setup_softmax(rf, torch, W):
+    """Two input/output sets (2 GiB), used alternately, so that no call finds
+    its operands in the 256 MB Infinity Cache left by the previous one."""
     c = W.CONFIGS[2]
     x = W.softmax_rows_input(2, c["rows"], c["cols"])
-    xd = torch.from_numpy(x).cuda()
-    yd = torch.empty_like(xd)
+    sets = []
+    for _ in range(2):
+        xd = torch.from_numpy(x).cuda()
+        sets.append((xd, torch.empty_like(xd)))
     nbytes = 2 * x.size * 4
-    return dict(fn=lambda: rf.rf_softmax_rows(xd, out=yd), work=nbytes, unit="GB/s", bound="hbm",
-                kernel_fn=None, keep=(xd, yd), cfg=c)
+    turn = [0]
+
+    def call():
+        xd, yd = sets[turn[0]]
+        turn[0] ^= 1
+        rf.rf_softmax_rows(xd, out=yd)
+    return dict(fn=call, work=nbytes, unit="GB/s", bound="hbm", keep=sets, cfg=c,
+                extra={"buffer_sets": 2})
 
 
 def setup_prefill(rf, torch, W):

@@ -64,6 +64,9 @@ namespace {
 #ifndef RF_ATT_SP
 #define RF_ATT_SP 1
 #endif
+#ifndef RF_ATT_HEAD_GROUP
+#define RF_ATT_HEAD_GROUP 2
+#endif
 #ifndef RF_ATT_SP_SCHED
 #define RF_ATT_SP_SCHED 1
 #endif
@@ -751,6 +754,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
 }
 
+// Work item of launch slot gi. With xcd_remap, consecutive slots (which the
+// hardware deals round-robin to the 8 XCDs) map to 8 contiguous ranges of
+// items, one per XCD, so that the query tiles of a head share one L2. Then
+// each complete block of head_group heads x n_qt query tiles is dispatched
+// query tile first, head second: the causal tiles of the block go heaviest
+// first across its heads (longest-first list scheduling, which keeps the
+// workgroups of an XCD finishing together), while only head_group heads' K/V
+// are live in that L2 at a time. A last partial block keeps its order.
+__device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_t per_xcd, int xcd_remap, int n_qt,
+                                             int head_group) {
+  const int64_t flat = xcd_remap ? (gi % 8) * per_xcd + gi / 8 : gi;
+  if (head_group <= 1) return flat;
+  const int64_t bsz = int64_t(head_group) * n_qt;
+  const int64_t b = flat / bsz, w = flat % bsz;
+  if ((b + 1) * bsz > n_items) return flat;
+  return (b * head_group + w % head_group) * n_qt + w / head_group;
+}
+
 // ---------------------------------------------------------------------------
 // Software-pipelined variant of the direct-to-LDS kernel.
 //
@@ -779,7 +800,7 @@ template <int D, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
-    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap) {
+    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group) {
   constexpr int BN = 64;
   constexpr int BM = 32 * NW;
   constexpr int KCH = D / 8;
@@ -822,7 +843,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tr_x = (lane >> 4) & 1, tr_y = lane & 3;
 
   for (int64_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
-    const int64_t item = xcd_remap ? (gi % 8) * per_xcd + gi / 8 : gi;
+    const int64_t item = work_item(gi, n_items, per_xcd, xcd_remap, n_qt, head_group);
     const int64_t bh = item / n_qt;
     const int qr = int(item % n_qt);
     const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
@@ -1485,7 +1506,7 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
     hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE>), dim3(grid), dim3(NW * 64), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
-                       block_mask, n_qt, n_items, xcd_remap);
+                       block_mask, n_qt, n_items, xcd_remap, causal ? RF_ATT_HEAD_GROUP : 1);
   else
     hipLaunchKernelGGL((attention_bf16_dma_kernel<D, NW, WPE, BN>), dim3(grid), dim3(NW * 64), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
