@@ -800,7 +800,8 @@ template <int D, int NW, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
-    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group) {
+    const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group,
+    int64_t item_base) {
   constexpr int BN = 64;
   constexpr int BM = 32 * NW;
   constexpr int KCH = D / 8;
@@ -842,8 +843,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int tr_row = 4 * h + ((lane & 15) >> 2);
   const int tr_x = (lane >> 4) & 1, tr_y = lane & 3;
 
-  for (int64_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
-    const int64_t item = work_item(gi, n_items, per_xcd, xcd_remap, n_qt, head_group);
+  // One work item per workgroup: items [item_base, item_base + gridDim.x) of
+  // this launch, permuted by work_item within the launch.
+  {
+    const int64_t item = item_base + work_item(blockIdx.x, n_items, per_xcd, xcd_remap, n_qt, head_group);
     const int64_t bh = item / n_qt;
     const int qr = int(item % n_qt);
     const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
@@ -1069,7 +1072,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     };
     f32x16_t s0[MB], s1[MB];
 
-    __syncthreads();  // the previous item's readers of every buffer are done
     bool m0 = false, m1 = false, m2 = false;
     int t0 = walk.next(0, &m0);
     if (t0 < kt_end) {
@@ -1118,22 +1120,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const float l_tot = pair_sum_halves(l_run);
     const float l_rtot = pair_sum_halves(l_rnd);
     const int qi = q0w + l32;
-    if (qi < Lq) {
-      const bool live = l_tot > 0.f;
-      const float inv = live ? 1.f / l_rtot : 0.f;
-      uint16_t* orow = o + (bh * Lq + qi) * int64_t(D);
+    const bool live = l_tot > 0.f;
+    const float inv = live ? 1.f / l_rtot : 0.f;
+    // Output: each wave's 32 rows are one contiguous block of O. Lanes l and
+    // l + 32 hold alternate 8-byte pieces of a row; one v_permlane32_swap per
+    // dword gives each lane a 16-byte run, which goes through this wave's own
+    // slice of the (now idle) K buffers so that every store instruction writes
+    // 1 KiB of consecutive bytes.
+    {
+      static_assert(NW * 32 <= 2 * BN, "output staging fits in the K buffers");
+      constexpr int OCH = D / 8;  // 16-byte chunks per row
+      uint16_t* stage = (wave < NW / 2 ? kb0 : kb1) + (wave % (NW / 2)) * 32 * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = 32 * db + 8 * r4 + 4 * h;
-          uint2 pkt;
-          pkt.x = cvt_pk_bf16(acc_o[db][4 * r4] * inv, acc_o[db][4 * r4 + 1] * inv);
-          pkt.y = cvt_pk_bf16(acc_o[db][4 * r4 + 2] * inv, acc_o[db][4 * r4 + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + d0) = pkt;
+        for (int pp = 0; pp < 2; ++pp) {
+          const int ra = 8 * pp, rb = 8 * pp + 4;  // d = 32 db + 16 pp + 4 h (+ 8 for rb)
+          const uint32_t ax = cvt_pk_bf16(acc_o[db][ra] * inv, acc_o[db][ra + 1] * inv);
+          const uint32_t ay = cvt_pk_bf16(acc_o[db][ra + 2] * inv, acc_o[db][ra + 3] * inv);
+          const uint32_t bx = cvt_pk_bf16(acc_o[db][rb] * inv, acc_o[db][rb + 1] * inv);
+          const uint32_t by = cvt_pk_bf16(acc_o[db][rb + 2] * inv, acc_o[db][rb + 3] * inv);
+          const auto sx = __builtin_amdgcn_permlane32_swap(ax, bx, false, false);
+          const auto sy = __builtin_amdgcn_permlane32_swap(ay, by, false, false);
+          const int c = 4 * db + 2 * pp + h;  // this lane now holds d = 8c .. 8c + 7
+          *reinterpret_cast<uint4*>(stage + l32 * D + 8 * (c ^ (l32 & (OCH - 1)))) =
+              make_uint4(sx[0], sy[0], sx[1], sy[1]);
         }
-      if (lse != nullptr && h == 0) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+      uint16_t* obase = o + (bh * Lq + q0w) * int64_t(D);
+#pragma unroll
+      for (int i = 0; i < 32 * OCH / 64; ++i) {
+        const int g = 64 * i + lane, row = g / OCH, c = g % OCH;
+        const uint4 x = *reinterpret_cast<const uint4*>(stage + row * D + 8 * (c ^ (row & (OCH - 1))));
+        if (q0w + row < Lq) *reinterpret_cast<uint4*>(obase + row * D + 8 * c) = x;
+      }
     }
+    if (lse != nullptr && h == 0 && qi < Lq) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
   }
 }
 
@@ -1502,12 +1523,19 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
   const int64_t cap = 1LL << 22;
   const unsigned grid = unsigned(n_items < cap ? n_items : cap);
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
-  if constexpr (SP)
-    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE>), dim3(grid), dim3(NW * 64), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
-                       block_mask, n_qt, n_items, xcd_remap, causal ? RF_ATT_HEAD_GROUP : 1);
-  else
+  if constexpr (SP) {
+    // One workgroup per item; more items than one grid allows go in chunks
+    // (then without the XCD placement, which assumes the whole item range).
+    for (int64_t base = 0; base < n_items; base += cap) {
+      const int64_t n = n_items - base < cap ? n_items - base : cap;
+      hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE>), dim3(unsigned(n)), dim3(NW * 64), 0, stream,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
+                         block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  } else
     hipLaunchKernelGGL((attention_bf16_dma_kernel<D, NW, WPE, BN>), dim3(grid), dim3(NW * 64), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
