@@ -64,6 +64,15 @@ namespace {
 #ifndef RF_ATT_SP
 #define RF_ATT_SP 1
 #endif
+#ifndef RF_ATT_SPLITEXP
+#define RF_ATT_SPLITEXP 1
+#endif
+#ifndef RF_ATT_SUMGUARD
+#define RF_ATT_SUMGUARD 1
+#endif
+#if RF_ATT_SPLITEXP && !RF_ATT_SUMGUARD
+#error "the split exponentials rely on the sum guard"
+#endif
 #ifndef RF_ATT_HEAD_GROUP
 #define RF_ATT_HEAD_GROUP 2
 #endif
@@ -123,6 +132,7 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
 // same rounded weights the MFMA consumed (O stays an exact convex combination of
 // V rows), while the LSE uses the sum of the unrounded weights.
 constexpr float kRescaleSlack = 8.f;
+constexpr float kSlackSum = 256.f;  // 2^kRescaleSlack
 
 // Raw buffer access: loads outside [0, bytes) return zero, so ragged tiles
 // need no predication.
@@ -908,7 +918,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         sacc[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[kstep]), sacc[mb]);
       }
     };
-    auto exp_tile = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8]) {
+    // P of a tile against the reference m_ref, with the tile's sums of P
+    // (exact, and of P as rounded for the P.V product) added to lt, ltr.
+    auto exp_tile = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8], float& lt, float& ltr) {
       const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -917,12 +929,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
           const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
           const uint32_t pp = cvt_pk_bf16(p0, p1);
-          l_run += p0 + p1;
-          l_rnd = add_bf16_pair(pp, l_rnd);
+          lt += p0 + p1;
+          ltr = add_bf16_pair(pp, ltr);
           pk[mb][r >> 1] = pp;
         }
     };
-    auto pv_mfmas = [&](const uint16_t* vs_, const uint32_t (&pk)[MB][8]) {
+    // P.V MFMAs i0 .. i1 - 1 of the tile (i = kstep * DB + db; K-steps 0 and 1
+    // use keys 0..31, i.e. the first half of P), V^T fragments read a window
+    // ahead; hook(j) runs after the j-th of them (vector work to interleave).
+    auto pv_range = [&](const uint16_t* vs_, const uint32_t (&pk)[MB][8], int i0, int i1, auto&& hook) {
       constexpr int VAHEAD = RF_ATT_VREAD_AHEAD > 0 ? RF_ATT_VREAD_AHEAD : 1;
       auto vread = [&](int i) {
         const int kstep = i / DB, db = i % DB;
@@ -934,16 +949,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       };
       uint4 vfrag[VAHEAD];
 #pragma unroll
-      for (int i = 0; i < VAHEAD; ++i) vfrag[i] = vread(i);
+      for (int i = 0; i < VAHEAD; ++i)
+        if (i0 + i < i1) vfrag[i] = vread(i0 + i);
 #pragma unroll
-      for (int i = 0; i < NPV; ++i) {
+      for (int i = i0; i < i1; ++i) {
         const int kstep = i / DB, db = i % DB;
         const int mb = kstep >> 1, r0 = (kstep & 1) * 4;
         const uint4 bp = make_uint4(pk[mb][r0], pk[mb][r0 + 1], pk[mb][r0 + 2], pk[mb][r0 + 3]);
-        const uint4 a = vfrag[i % VAHEAD];
-        if (i + VAHEAD < NPV) vfrag[i % VAHEAD] = vread(i + VAHEAD);
+        const uint4 a = vfrag[(i - i0) % VAHEAD];
+        if (i + VAHEAD < i1) vfrag[(i - i0) % VAHEAD] = vread(i + VAHEAD);
         acc_o[db] = mfma32(as_bf16x8(a), as_bf16x8(bp), acc_o[db]);
+        hook(i - i0);
       }
+    };
+    auto pv_mfmas = [&](const uint16_t* vs_, const uint32_t (&pk)[MB][8]) {
+      pv_range(vs_, pk, 0, NPV, [](int) {});
     };
     // Scores this wave must not see -> -inf: keys past the row's last key (causal
     // diagonal, sequence end), and the whole tile when the wave's block-mask row
@@ -988,12 +1008,127 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
     };
+    // Commit a tile's P. It was formed against m_ref without looking at the
+    // tile's maximum: each lane's sum of its P bounds every one of them, so
+    // while that sum stays within 2^kRescaleSlack (and the row has a
+    // reference at all) the lazy-rescale bound holds and P is kept. Otherwise
+    // the row maximum decides as in the lazy rescale: if it exceeds the
+    // reference by more than the slack, the reference moves to it, the state
+    // so far is rescaled and the tile's P is formed again.
+    auto commit_tile = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8], float lt, float ltr) {
+      const bool suspect = !(lt <= kSlackSum) || m_ref == kNegInf;
+      if (__builtin_amdgcn_ballot_w64(suspect)) {
+        bool moved = false;
+        const float alpha = tile_max(st, &moved);
+        if (moved) {
+          rescale(alpha);
+          lt = 0.f;
+          ltr = 0.f;
+          exp_tile(st, pk, lt, ltr);
+        }
+      }
+      l_run += lt;
+      l_rnd += ltr;
+    };
 
+    // One score pair (keys 2r, 2r + 1 of 32-key block mb) of P against mu.
+    auto exp_pair = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8], int mb, int r, float mu, float& lt,
+                        float& ltr) {
+      const float p0 = fast_exp2(fmaf(st[mb][2 * r], c_log2, -mu));
+      const float p1 = fast_exp2(fmaf(st[mb][2 * r + 1], c_log2, -mu));
+      const uint32_t pp = cvt_pk_bf16(p0, p1);
+      lt += p0 + p1;
+      ltr = add_bf16_pair(pp, ltr);
+      pk[mb][r] = pp;
+    };
+    // commit_tile for one 32-key half of the tile: the guard looks at this
+    // half's sums, the reference follows the whole tile's maximum, and only
+    // this half's P is formed again. Halves committed earlier are already in
+    // O and the sums, and the rescale covers them.
+    auto commit_half = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8], int mb, float lt, float ltr) {
+      const bool suspect = !(lt <= kSlackSum) || m_ref == kNegInf;
+      if (__builtin_amdgcn_ballot_w64(suspect)) {
+        bool moved = false;
+        const float alpha = tile_max(st, &moved);
+        if (moved) {
+          rescale(alpha);
+          lt = 0.f;
+          ltr = 0.f;
+          const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) exp_pair(st, pk, mb, r, mu, lt, ltr);
+        }
+      }
+      l_run += lt;
+      l_rnd += ltr;
+    };
+#if RF_ATT_SPLITEXP
+    static_assert(MB == 2, "two halves per tile");
+    // Steady-state step with the exponentials split across both phases:
+    //   phase A : S(next) MFMAs     with the exponentials of keys 0..31
+    //   phase B1: P.V keys 0..31    with the exponentials of keys 32..63
+    //   phase B2: P.V keys 32..63
+    auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
+                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next) {
+      uint32_t pk[MB][8];
+      float lt0 = 0.f, ltr0 = 0.f, lt1 = 0.f, ltr1 = 0.f;
+      {
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_next[a][r] = 0.f;
+        constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
+        auto kread = [&](int i) {
+          const int kstep = i / MB, mb = i % MB;
+          const int row = 32 * mb + l32;
+          return *reinterpret_cast<const uint4*>(ks_next + row * D + 8 * SW::k_slot(row, 2 * kstep + h));
+        };
+        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+        uint4 kfrag[KAHEAD];
+#pragma unroll
+        for (int i = 0; i < KAHEAD; ++i) kfrag[i] = kread(i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const int kstep = i / MB, mb = i % MB;
+          const uint4 a = kfrag[i % KAHEAD];
+          if (i + KAHEAD < NS) kfrag[i % KAHEAD] = kread(i + KAHEAD);
+          s_next[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[kstep]), s_next[mb]);
+#pragma unroll
+          for (int r = i * 8 / NS; r < (i + 1) * 8 / NS; ++r) exp_pair(s_cur, pk, 0, r, mu, lt0, ltr0);
+#if RF_ATT_SP_SCHED
+          __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[0][i]));
+      asm volatile("" ::"v"(lt0), "v"(ltr0));
+      commit_half(s_cur, pk, 0, lt0, ltr0);
+      mask_tile(s_next, kt_next, mine_next);
+      {
+        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
+        constexpr int NB1 = NPV / 2;
+        pv_range(vs_cur, pk, 0, NB1, [&](int j) {
+#pragma unroll
+          for (int r = j * 8 / NB1; r < (j + 1) * 8 / NB1; ++r) exp_pair(s_cur, pk, 1, r, mu, lt1, ltr1);
+#if RF_ATT_SP_SCHED
+          __builtin_amdgcn_sched_barrier(0);
+#endif
+        });
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[1][i]));
+      asm volatile("" ::"v"(lt1), "v"(ltr1));
+      commit_half(s_cur, pk, 1, lt1, ltr1);
+      pv_range(vs_cur, pk, NPV / 2, NPV, [](int) {});
+    };
+#else
     // One steady-state step: current tile (scores s_cur, V in vs_cur), next tile
     // (K in ks_next, scores into s_next).
     auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
                     f32x16_t (&s_next)[MB], int kt_next, bool mine_next) {
       uint32_t pk[MB][8];
+      float lt = 0.f, ltr = 0.f;
       // Phase A: score product of the next tile with the exponentials of this
       // one, written as NS chunks of one MFMA plus its share of the vector work
       // (fenced so the compiler keeps the interleave).
@@ -1028,8 +1163,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
               const float p0 = fast_exp2(fmaf(s_cur[cb][r], c_log2, -mu));
               const float p1 = fast_exp2(fmaf(s_cur[cb][r + 1], c_log2, -mu));
               const uint32_t pp = cvt_pk_bf16(p0, p1);
-              l_run += p0 + p1;
-              l_rnd = add_bf16_pair(pp, l_rnd);
+              lt += p0 + p1;
+              ltr = add_bf16_pair(pp, ltr);
               pk[cb][r >> 1] = pp;
             }
           }
@@ -1044,7 +1179,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[mb][i]));
-      asm volatile("" ::"v"(l_run), "v"(l_rnd));
+      asm volatile("" ::"v"(lt), "v"(ltr));
+#if RF_ATT_SUMGUARD
+      commit_tile(s_cur, pk, lt, ltr);
+      mask_tile(s_next, kt_next, mine_next);
+      // Phase B: P.V product of this tile.
+      pv_mfmas(vs_cur, pk);
+#else
+      l_run += lt;
+      l_rnd += ltr;
       mask_tile(s_next, kt_next, mine_next);
       // Phase B: P.V product of this tile with the row maximum of the next one.
       pv_mfmas(vs_cur, pk);
@@ -1063,11 +1206,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
 #endif
       if (moved) rescale(alpha);
+#endif
     };
+#endif
     // The last tile: exponentials and P.V product only.
     auto finish = [&](const uint16_t* vs_cur, const f32x16_t (&s_cur)[MB]) {
       uint32_t pk[MB][8];
-      exp_tile(s_cur, pk);
+      float lt = 0.f, ltr = 0.f;
+      exp_tile(s_cur, pk, lt, ltr);
+#if RF_ATT_SUMGUARD
+      commit_tile(s_cur, pk, lt, ltr);
+#else
+      l_run += lt;
+      l_rnd += ltr;
+#endif
       pv_mfmas(vs_cur, pk);
     };
     f32x16_t s0[MB], s1[MB];
