@@ -254,6 +254,53 @@ def test_attention_bf16_rising_scores(rf_gpu):
     assert_close(host_f64(lse), ref_lse, 1e-3, "LSE")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_bf16_jumps_inside_tiles(rf_gpu, d, causal):
+    """Scores that jump by far more than the rescale slack (2^8) in the second
+    32-key half of a tile, in the first half of the next one, and in the last
+    tile: the reference must move after part of a tile is already in O."""
+    L = 256
+    q = np.full((1, 2, L, d), 0.5, np.float32)
+    k = np.zeros((1, 2, L, d), np.float32)
+    k[:, :, 96:128] = 2.0      # tile 1, keys 32..63 of the tile
+    k[:, :, 128:160] = 4.0     # tile 2, keys 0..31
+    k[:, :, 224:256] = 6.0     # tile 3 (last), keys 32..63
+    v = _normal(112, 2, (1, 2, L, d), "f32")
+    qb, kb, vb = (W.f32_to_bf16_bits(a) for a in (q, k, v))
+    note(f"jumps inside tiles d={d} causal={causal}")
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), causal=causal)
+    ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a) for a in (qb, kb, vb)), 1 / math.sqrt(d), causal)
+    assert_close(host_f64(o), ref_o, 1e-2, "O")
+    assert_close(host_f64(lse), ref_lse, 1e-3, "LSE")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_bf16_reference_from_a_later_tile(rf_gpu, d):
+    """A wave whose first visited key tile is hidden by its block-mask row has no
+    exponent reference yet; its next tile's scores (about -220 in log2 units)
+    would all underflow against a zero reference. Rows 0..63 see only key tile
+    1, whose keys are identical: O is the mean of those V rows."""
+    import torch
+    L = 256
+    q = np.ones((1, 1, L, d), np.float32)
+    k = np.ones((1, 1, L, d), np.float32)
+    k[:, :, 64:128] = -1.2 * 128 / d
+    v = _normal(113, 2, (1, 1, L, d), "f32")
+    bm = np.zeros((4, 4), np.uint8)
+    bm[0, 1] = 1
+    bm[1, 0] = bm[1, 1] = 1
+    bm[2, 2] = bm[3, 3] = 1
+    qb, kb, vb = (W.f32_to_bf16_bits(a) for a in (q, k, v))
+    note(f"reference from a later tile d={d}")
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(qb), dev_bf16(kb), dev_bf16(vb), scale=1.0,
+                                     block_mask=torch.from_numpy(bm).cuda())
+    ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a) for a in (qb, kb, vb)), 1.0, False, bm)
+    assert np.all(np.isfinite(ref_lse)) and ref_lse[0, 0, 0] < -100
+    assert_close(host_f64(o), ref_o, 1e-2, "O")
+    assert_close(host_f64(lse), ref_lse, 1e-3, "LSE")
+
+
 def test_attention_bf16_deterministic(rf_gpu):
     q, k, v = (dev_bf16(_normal(110, i, (2, 4, 700, 128), "bf16")) for i in range(3))
     note("attention determinism")
