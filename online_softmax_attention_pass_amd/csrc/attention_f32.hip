@@ -2,17 +2,20 @@
 // RedFuser page, 3. Contributions clés; online rescale as on the FLASHLIGHT
 // page, Metodologia 3). Used for fp32 inputs with any head dim d <= 128.
 //
-// A workgroup of 256 lanes owns BM = 32 query rows of one (b, h) and sweeps
-// the visible key tiles of BN = 32 keys. Lane (r, p) = (t / 8, t % 8) holds
-// query row r: it scores keys p, p + 8, p + 16, p + 24 of the tile and
-// accumulates output columns p, p + 8, ... of row r, so the running (m, l)
-// of a row lives in the 8 lanes that share it. Masked key tiles are skipped
-// before any load (STOF page, Énoncé du problème / Méthodologie 1: skip rather
-// than compute and reset); only tiles that straddle the causal diagonal or
-// the end of the keys are masked per element.
+// A workgroup of 256 lanes owns BM = 16 query rows of one (b, h) and sweeps
+// the visible key tiles of BN = 32 keys. Lane (r, p) = (t / 16, t % 16) holds
+// query row r: it scores keys p and p + 16 of the tile and accumulates the
+// output columns [p * DMAX / 16, (p + 1) * DMAX / 16) of row r, so the running
+// (m, l) of a row lives in the 16 lanes that share it. Masked key tiles are
+// skipped before any load (STOF page, Énoncé du problème / Méthodologie 1:
+// skip rather than compute and reset); only tiles that straddle the causal
+// diagonal or the end of the keys are masked per element.
 //
-// This is a small-problem, fp32-exact path: scores and accumulators are fp32
-// FMA chains; matrix cores are used by the bf16 path.
+// This is a small-problem, fp32-exact path, shaped for latency: every dot
+// product runs as four independent partial chains over 16-byte LDS reads
+// (rows are zero-padded to DMAX so the loops have fixed trip counts), and P.V
+// keeps one independent accumulator per output column. Matrix cores are used
+// by the bf16 path.
 #include <stdint.h>
 
 #include "rf_internal.h"
@@ -20,7 +23,7 @@
 namespace rf {
 namespace {
 
-constexpr int kBM = 32, kBN = 32, kMaskTile = 64;
+constexpr int kBM = 16, kBN = 32, kMaskTile = 64;
 
 template <int DMAX>
 __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
@@ -29,15 +32,19 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
                                                             float scale_log2, int causal,
                                                             const uint8_t* __restrict__ block_mask, int n_qt,
                                                             int64_t n_items) {
-  constexpr int DP = DMAX + 1;  // padded row: lanes of one row hit distinct banks
-  constexpr int NACC = DMAX / 8;
-  __shared__ float Qs[kBM][DP];
-  __shared__ float Ks[kBN][DP];
-  __shared__ float Vs[kBN][DP];
-  __shared__ float Ps[kBM][kBN + 1];
+  // Rows padded by 4 floats: 16-byte aligned, and the 16 key rows one
+  // instruction reads start 4 banks apart.
+  constexpr int DP = DMAX + 4;
+  constexpr int NC = DMAX / 16;  // output columns per lane
+  static_assert(DMAX % 16 == 0, "column split");
+  __shared__ __align__(16) float Qs[kBM][DP];
+  __shared__ __align__(16) float Ks[kBN][DP];
+  __shared__ __align__(16) float Vs[kBN][DP];
+  __shared__ __align__(16) float Ps[kBM][kBN];
 
   const int t = threadIdx.x;
-  const int r = t >> 3, p = t & 7;
+  const int r = t >> 4, p = t & 15;
+  const int c0 = p * NC;  // first output column of this lane
   const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
   const int n_kt = (Lk + kBN - 1) / kBN;
 
@@ -57,9 +64,9 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
 
     const int qi = q0 + r;  // this lane's query row
     float m = kNegInf, l = 0.f;
-    float acc[NACC];
+    float acc[NC];
 #pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] = 0.f;
+    for (int i = 0; i < NC; ++i) acc[i] = 0.f;
 
     // Last key any row of this tile may see under the causal rule.
     const int64_t causal_last = int64_t(min(q0 + kBM, Lq) - 1) + (Lk - Lq);
@@ -78,39 +85,64 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
       }
       __syncthreads();
 
-      float s[4];
+      // Scores of keys p and p + 16: four partial sums each over 16-byte reads.
+      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < DMAX; e += 4) {
+        const float4 qv = *reinterpret_cast<const float4*>(&Qs[r][e]);
+        const float4 ka = *reinterpret_cast<const float4*>(&Ks[p][e]);
+        const float4 kb = *reinterpret_cast<const float4*>(&Ks[p + 16][e]);
+        pa[0] = fmaf(qv.x, ka.x, pa[0]);
+        pa[1] = fmaf(qv.y, ka.y, pa[1]);
+        pa[2] = fmaf(qv.z, ka.z, pa[2]);
+        pa[3] = fmaf(qv.w, ka.w, pa[3]);
+        pb[0] = fmaf(qv.x, kb.x, pb[0]);
+        pb[1] = fmaf(qv.y, kb.y, pb[1]);
+        pb[2] = fmaf(qv.z, kb.z, pb[2]);
+        pb[3] = fmaf(qv.w, kb.w, pb[3]);
+      }
+      float s[2];
+      const float dots[2] = {(pa[0] + pa[1]) + (pa[2] + pa[3]), (pb[0] + pb[1]) + (pb[2] + pb[3])};
       float bm = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = p + 8 * j;
-        float dot = 0.f;
-        for (int e = 0; e < d; ++e) dot = fmaf(Qs[r][e], Ks[c][e], dot);
-        const int kj = k0 + c;
+      for (int j = 0; j < 2; ++j) {
+        const int kj = k0 + p + 16 * j;
         const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= int64_t(qi) + (Lk - Lq));
-        s[j] = vis ? dot * scale_log2 : kNegInf;
+        s[j] = vis ? dots[j] * scale_log2 : kNegInf;
         bm = fmaxf(bm, s[j]);
       }
-      bm = group_max<8>(bm);
+      bm = group_max<16>(bm);
       const float mn = fmaxf(m, bm);
       const float mu = (mn == kNegInf) ? 0.f : mn;
       const float alpha = fast_exp2(m - mu);
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pj = fast_exp2(s[j] - mu);
-        Ps[r][p + 8 * j] = pj;
-        ps += pj;
-      }
-      ps = group_sum<8>(ps);
-      l = l * alpha + ps;
+      const float p0 = fast_exp2(s[0] - mu), p1 = fast_exp2(s[1] - mu);
+      Ps[r][p] = p0;
+      Ps[r][p + 16] = p1;
+      l = l * alpha + group_sum<16>(p0 + p1);
       m = mn;
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < NACC; ++i) {
-        const int e = p + 8 * i;
-        float a = acc[i] * alpha;
-        for (int c = 0; c < kBN; ++c) a = fmaf(Ps[r][c], Vs[c][e], a);
-        acc[i] = a;
+      for (int i = 0; i < NC; ++i) acc[i] *= alpha;
+#pragma unroll 8
+      for (int c = 0; c < kBN; ++c) {
+        const float pc = Ps[r][c];
+        if constexpr (NC % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < NC; i += 4) {
+            const float4 vv = *reinterpret_cast<const float4*>(&Vs[c][c0 + i]);
+            acc[i] = fmaf(pc, vv.x, acc[i]);
+            acc[i + 1] = fmaf(pc, vv.y, acc[i + 1]);
+            acc[i + 2] = fmaf(pc, vv.z, acc[i + 2]);
+            acc[i + 3] = fmaf(pc, vv.w, acc[i + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NC; i += 2) {  // NC = 2: 8-byte aligned pairs
+            const float2 vv = *reinterpret_cast<const float2*>(&Vs[c][c0 + i]);
+            acc[i] = fmaf(pc, vv.x, acc[i]);
+            acc[i + 1] = fmaf(pc, vv.y, acc[i + 1]);
+          }
+        }
       }
     }
 
@@ -119,10 +151,8 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
       const float inv = live ? 1.f / l : 0.f;
       float* orow = o + (bh * Lq + qi) * int64_t(d);
 #pragma unroll
-      for (int i = 0; i < NACC; ++i) {
-        const int e = p + 8 * i;
-        if (e < d) orow[e] = acc[i] * inv;
-      }
+      for (int i = 0; i < NC; ++i)
+        if (c0 + i < d) orow[c0 + i] = acc[i] * inv;
       if (lse != nullptr && p == 0) lse[bh * Lq + qi] = live ? (m + fast_log2(l)) * kLn2 : kNegInf;
     }
   }
