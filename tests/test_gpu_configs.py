@@ -117,3 +117,42 @@ def test_config4_decode(rf_gpu):
         refs.append(ref_o[0, 0])
     _report(f"config4 ({len(heads)} heads)", worst_o, worst_l, np.concatenate(refs))
     assert worst_o <= 1e-2 and worst_l <= 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Long key sequences: large in-head offsets, many tiles and splits, ragged ends
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_bf16_long_keys(rf_gpu, d):
+    """600,007 keys (ragged), 200 query rows, causal (bottom-right): every row
+    sweeps ~9,400 key tiles; sampled rows at tile edges against the oracle."""
+    B, H, Lq, Lk = 1, 1, 200, 600_007
+    q = W.normal_tensor(120, W.TID_Q, B, H, Lq, d, "bf16")
+    k = W.normal_tensor(120, W.TID_K, B, H, Lk, d, "bf16")
+    v = W.normal_tensor(120, W.TID_V, B, H, Lk, d, "bf16")
+    scale = 1 / math.sqrt(d)
+    note(f"long keys d={d} Lk={Lk}")
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, causal=True)
+    rows = [0, 31, 32, 63, 64, 127, 128, 199]
+    ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a) for a in (q, k, v)), scale, True, q_rows=rows)
+    got_o = host_f64(o)[:, :, rows]
+    got_l = host_f64(lse)[:, :, rows]
+    e_o = assert_close(got_o, ref_o, 1e-2, "long keys O")
+    e_l = assert_close(got_l, ref_lse, 1e-3, "long keys LSE")
+    _report(f"long keys d{d}", e_o, e_l, ref_o)
+
+
+def test_decode_long_keys(rf_gpu):
+    """2,000,003 keys split 61 ways (ragged last split), checked whole."""
+    B, H, Lk, d, S = 1, 1, 2_000_003, 128, 61
+    q = W.normal_tensor(121, W.TID_Q, B, H, 1, d, "bf16")
+    k = W.normal_tensor(121, W.TID_K, B, H, Lk, d, "bf16")
+    v = W.normal_tensor(121, W.TID_V, B, H, Lk, d, "bf16")
+    scale = 1 / math.sqrt(d)
+    note(f"decode long keys Lk={Lk} S={S}")
+    o, lse = rf_gpu.rf_attention_decode_splitkv(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=scale, num_splits=S)
+    ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a) for a in (q, k, v)), scale)
+    e_o = assert_close(host_f64(o), ref_o, 1e-2, "decode long O")
+    e_l = assert_close(host_f64(lse), ref_lse[:, :, 0], 1e-3, "decode long LSE")
+    _report("decode long keys", e_o, e_l, ref_o)
