@@ -111,11 +111,19 @@ def logsumexp_rows(x: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def element_mask(Lq: int, Lk: int, causal: bool, block_mask=None, tile: int = 64,
-                 q_rows=None) -> np.ndarray:
+                 q_rows=None, tile_bits=None) -> np.ndarray:
     """Boolean [rows, Lk]: which keys each query row may attend to.
 
     visible(i, j) = (not causal or j <= i + Lk - Lq)
                     and (block_mask is None or block_mask[i // tile, j // tile] != 0)
+
+    With ``tile_bits`` (uint64 [n_row_tiles, n_col_tiles, 64]; STOF page,
+    Méthodologie 1, two-level storage format: "full" and "partial" outer tiles,
+    64-bit element bitmaps inside the partial ones) the kind block_mask[I, J]
+    decides: 1 = full tile, 0 = empty, any other value = partial, where row i
+    sees key j iff bit (j mod 64) of word tile_bits[I, J, i mod 64] is set (the
+    64 words of a tile are its rows; the page groups the same 4096 bits by 8x8
+    blocks).
     """
     i = np.arange(Lq) if q_rows is None else np.asarray(q_rows)
     i = i[:, None]
@@ -125,7 +133,13 @@ def element_mask(Lq: int, Lk: int, causal: bool, block_mask=None, tile: int = 64
         vis &= j <= i + (Lk - Lq)
     if block_mask is not None:
         bm = np.asarray(block_mask)
-        vis &= bm[i // tile, j // tile] != 0
+        kind = bm[i // tile, j // tile]
+        if tile_bits is None:
+            vis &= kind != 0
+        else:
+            words = np.asarray(tile_bits, dtype=np.uint64)[i // tile, j // tile, i % tile]
+            bit = (words >> (j % tile).astype(np.uint64)) & np.uint64(1)
+            vis &= (kind == 1) | ((kind != 0) & (bit == 1))
     return vis
 
 
@@ -147,7 +161,7 @@ def _attention_head(q, k, v, scale, visible):
 
 
 def attention(q, k, v, scale: float, causal: bool = False, block_mask=None,
-              tile: int = 64, q_rows=None):
+              tile: int = 64, q_rows=None, tile_bits=None):
     """Multi-head attention with the masked safe softmax, in fp64.
 
     q: [B, H, Lq, d]; k, v: [B, H, Lk, d] (any real dtype; widened to fp64).
@@ -160,7 +174,7 @@ def attention(q, k, v, scale: float, causal: bool = False, block_mask=None,
     B, H, Lq, d = q.shape
     Lk = k.shape[2]
     rows = np.arange(Lq) if q_rows is None else np.asarray(q_rows)
-    vis = element_mask(Lq, Lk, causal, block_mask, tile, rows)
+    vis = element_mask(Lq, Lk, causal, block_mask, tile, rows, tile_bits)
     O = np.zeros((B, H, len(rows), v.shape[3]))
     LSE = np.full((B, H, len(rows)), NEG_INF)
     for b in range(B):

@@ -527,3 +527,174 @@ def test_merge_mutants_are_caught(kind):
               and pin_split_merge_equals_unsplit(O.decode_splitkv_partials, fn, _oracle_attn))
     assert not ok
     assert pin_merge_golden(_merge_mutant("none")) and pin_merge_monoid(_merge_mutant("none"))
+
+
+# ---------------------------------------------------------------------------
+# element bitmaps inside partial tiles (STOF two-level format)
+# ---------------------------------------------------------------------------
+
+def _bitmap_case(seed, Lq=130, Lk=200):
+    r = np.random.default_rng(seed)
+    nI, nJ = -(-Lq // 64), -(-Lk // 64)
+    kinds = r.choice(np.array([0, 1, 2, 7], np.uint8), size=(nI, nJ))   # 7: any other nonzero kind is partial
+    bits = r.integers(0, 2 ** 63, size=(nI, nJ, 64), dtype=np.uint64) * np.uint64(2) + \
+        r.integers(0, 2, size=(nI, nJ, 64), dtype=np.uint64)
+    return kinds, bits
+
+
+def _decode_python(Lq, Lk, causal, kinds, bits):
+    """The bitmap definition written out with Python integers, element by element."""
+    out = np.zeros((Lq, Lk), dtype=bool)
+    for i in range(Lq):
+        for j in range(Lk):
+            kind = int(kinds[i // 64][j // 64])
+            if kind == 0:
+                vis = False
+            elif kind == 1:
+                vis = True
+            else:
+                word = int(bits[i // 64][j // 64][i % 64])
+                vis = (word >> (j % 64)) & 1 == 1
+            if causal and j > i + (Lk - Lq):
+                vis = False
+            out[i, j] = vis
+    return out
+
+
+def pin_bitmap_bruteforce(mask_fn):
+    for seed, causal in ((21, False), (22, True)):
+        kinds, bits = _bitmap_case(seed)
+        if not np.array_equal(mask_fn(130, 200, causal, kinds, bits), _decode_python(130, 200, causal, kinds, bits)):
+            return False
+    return True
+
+
+def pin_bitmap_all_ones_is_full(mask_fn):
+    kinds, _ = _bitmap_case(23)
+    ones = np.full(kinds.shape + (64,), np.uint64(2 ** 64 - 1))
+    full = np.where(kinds != 0, 1, 0).astype(np.uint8)
+    return bool(np.array_equal(mask_fn(130, 200, False, kinds, ones), mask_fn(130, 200, False, full, ones)))
+
+
+def pin_bitmap_causal_diagonal(mask_fn):
+    """Lower-triangular bitmaps on the diagonal tiles, full tiles below, empty above:
+    without the causal flag this is exactly the causal mask."""
+    n = 4
+    kinds = np.tril(np.ones((n, n), np.uint8)) + np.eye(n, dtype=np.uint8)     # 1 below, 2 on the diagonal
+    tri = np.array([(1 << (r + 1)) - 1 for r in range(64)], dtype=np.uint64)   # row r sees keys 0..r
+    bits = np.zeros((n, n, 64), np.uint64)
+    for t in range(n):
+        bits[t, t] = tri
+    got = mask_fn(256, 256, False, kinds, bits)
+    return bool(np.array_equal(got, O.element_mask(256, 256, True)))
+
+
+def pin_bitmap_single_bit(mask_fn):
+    kinds = np.full((3, 3), 2, np.uint8)
+    bits = np.zeros((3, 3, 64), np.uint64)
+    bits[1, 2, 5] = np.uint64(1) << np.uint64(9)
+    got = mask_fn(192, 192, False, kinds, bits)
+    want = np.zeros((192, 192), bool)
+    want[64 + 5, 128 + 9] = True
+    return bool(np.array_equal(got, want))
+
+
+def _oracle_mask(Lq, Lk, causal, kinds, bits):
+    return O.element_mask(Lq, Lk, causal, kinds, 64, None, bits)
+
+
+def test_bitmap_mask_pins():
+    assert pin_bitmap_bruteforce(_oracle_mask)
+    assert pin_bitmap_all_ones_is_full(_oracle_mask)
+    assert pin_bitmap_causal_diagonal(_oracle_mask)
+    assert pin_bitmap_single_bit(_oracle_mask)
+
+
+def test_bitmap_attention_matches_python_masked_attention():
+    """Attention under a bitmap mask against pure-Python loops over the
+    decoded element mask (exp via math.exp, sums via math.fsum)."""
+    Lq, Lk, d = 70, 90, 3
+    r = np.random.default_rng(24)
+    kinds, bits = _bitmap_case(25, Lq, Lk)
+    kinds[0, 0] = 2
+    q, k, v = r.normal(size=(1, 1, Lq, d)), r.normal(size=(1, 1, Lk, d)), r.normal(size=(1, 1, Lk, d))
+    o, lse = O.attention(q, k, v, 0.4, True, kinds, tile_bits=bits)
+    vis = _decode_python(Lq, Lk, True, kinds, bits)
+    for i in range(Lq):
+        s = [0.4 * math.fsum(q[0, 0, i, e] * k[0, 0, j, e] for e in range(d)) for j in range(Lk) if vis[i, j]]
+        js = [j for j in range(Lk) if vis[i, j]]
+        if not s:
+            assert lse[0, 0, i] == NEG_INF and np.all(o[0, 0, i] == 0)
+            continue
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        W_ = math.fsum(w)
+        ref = [math.fsum(wi * v[0, 0, j, e] for wi, j in zip(w, js)) / W_ for e in range(d)]
+        assert np.allclose(o[0, 0, i], ref, rtol=1e-12, atol=1e-13)
+        assert abs(lse[0, 0, i] - (m + math.log(W_))) <= 1e-12
+
+
+def _mask_mutant(kind):
+    def fn(Lq, Lk, causal, kinds, bits):
+        i = np.arange(Lq)[:, None]
+        j = np.arange(Lk)[None, :]
+        vis = np.ones((Lq, Lk), bool)
+        if causal:
+            vis &= j <= i + (Lk - Lq)
+        kk = np.asarray(kinds)[i // 64, j // 64]
+        if kind == "transposed_words":
+            words = np.asarray(bits, np.uint64)[i // 64, j // 64, j % 64]
+            bit = (words >> (i % 64).astype(np.uint64)) & np.uint64(1)
+        elif kind == "bit_off_by_one":
+            words = np.asarray(bits, np.uint64)[i // 64, j // 64, i % 64]
+            bit = (words >> ((j + 1) % 64).astype(np.uint64)) & np.uint64(1)
+        elif kind == "msb_first":
+            words = np.asarray(bits, np.uint64)[i // 64, j // 64, i % 64]
+            bit = (words >> (63 - j % 64).astype(np.uint64)) & np.uint64(1)
+        else:
+            words = np.asarray(bits, np.uint64)[i // 64, j // 64, i % 64]
+            bit = (words >> (j % 64).astype(np.uint64)) & np.uint64(1)
+        if kind == "partial_as_full":
+            vis &= kk != 0
+        elif kind == "only_kind_two_partial":
+            vis &= (kk == 1) | ((kk == 2) & (bit == 1))
+        elif kind == "full_uses_bits":
+            vis &= (kk != 0) & (bit == 1)
+        else:
+            vis &= (kk == 1) | ((kk != 0) & (bit == 1))
+        return vis
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["transposed_words", "bit_off_by_one", "msb_first", "partial_as_full",
+                                  "only_kind_two_partial", "full_uses_bits"])
+def test_bitmap_mutants_are_caught(kind):
+    fn = _mask_mutant(kind)
+    ok = (pin_bitmap_bruteforce(fn) and pin_bitmap_all_ones_is_full(fn) and pin_bitmap_causal_diagonal(fn)
+          and pin_bitmap_single_bit(fn))
+    assert not ok
+    none = _mask_mutant("none")
+    assert pin_bitmap_bruteforce(none) and pin_bitmap_causal_diagonal(none) and pin_bitmap_single_bit(none)
+
+
+def test_bitmap_workload_mask():
+    """The extension workload's mask: every row sees exactly its 512-key causal
+    window, plus whole random tiles strictly below the window's tile band."""
+    kinds, bits = W.extension_bitmap_mask()
+    n = kinds.shape[0]
+    wt = 8
+    n_cand = sum(max(0, I - wt) for I in range(n))
+    random_tiles = int(((kinds == 1) & np.tril(np.ones((n, n), bool), k=-(wt + 1))).sum())
+    assert random_tiles == round(0.10 * n_cand)
+    assert int((kinds == 2).sum()) == n + (n - wt)           # diagonal tiles + the window's lower-edge tiles
+    # full and empty tiles carry no bits; partial tiles have some but not all
+    assert not bits[kinds != 2].any()
+    part = bits[kinds == 2]
+    assert np.all(part.any(axis=-1)) and not np.all(part == np.uint64(2 ** 64 - 1))
+    rows = [0, 63, 64, 511, 512, 1000, 8191]
+    vis = O.element_mask(8192, 8192, False, kinds, 64, rows, bits)
+    for i, vr in zip(rows, vis):
+        window = set(range(max(0, i - 511), i + 1))
+        got = set(np.nonzero(vr)[0].tolist())
+        assert window <= got
+        assert all(kinds[i // 64, j // 64] == 1 and j // 64 <= i // 64 - wt - 1 for j in got - window)

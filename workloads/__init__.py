@@ -158,6 +158,55 @@ def window_random_block_mask(seed: int, n_tiles: int, window_tiles: int = 8,
     return m
 
 
+def window_bitmap_mask(seed: int, L: int, window: int = 512, frac: float = 0.10):
+    """Tile kinds uint8 [n, n] and row bitmaps uint64 [n, n, 64] (n = ceil(L / 64)).
+
+    Row i sees key j when i - window < j <= i (an element-level causal sliding
+    window), plus every key of exactly round(frac * N) 64x64 tiles drawn
+    uniformly without replacement from the N tiles wholly below the window's
+    tile band (J <= I - window / 64 - 1). Tiles whose elements are all visible
+    get kind 1, none kind 0, the rest kind 2 with word r of the tile holding
+    row r's visibility of its 64 keys (bit j).
+    """
+    n = math.ceil(L / MASK_TILE)
+    wt = window // MASK_TILE
+    kinds = np.zeros((n, n), dtype=np.uint8)
+    bits = np.zeros((n, n, MASK_TILE), dtype=np.uint64)
+    r = np.arange(MASK_TILE)[:, None]
+    c = np.arange(MASK_TILE)[None, :]
+    weights = (np.uint64(1) << np.arange(MASK_TILE, dtype=np.uint64))
+    for I in range(n):
+        for J in range(max(0, I - wt), I + 1):
+            i = I * MASK_TILE + r
+            j = J * MASK_TILE + c
+            vis = (j <= i) & (j > i - window) & (i < L) & (j < L)
+            if vis.all():
+                kinds[I, J] = 1
+            elif vis.any():
+                kinds[I, J] = 2
+                bits[I, J] = (vis.astype(np.uint64) * weights).sum(axis=1, dtype=np.uint64)
+    cand_i, cand_j = np.nonzero(np.tril(np.ones((n, n), bool), k=-(wt + 1)))
+    n_pick = int(round(frac * len(cand_i)))
+    if n_pick:
+        pick = rng(seed, TID_MASK).choice(len(cand_i), size=n_pick, replace=False)
+        kinds[cand_i[pick], cand_j[pick]] = 1
+    return kinds, bits
+
+
+# Extension beyond the five specified workloads: element-level sparsity inside
+# partial tiles (the STOF two-level format), at the block-sparse shape.
+EXTENSION_CONFIGS = {
+    "bitmap": dict(name="bitmap_sparse_bf16_B2_H16_L8192_d64", kind="attention", dtype="bf16",
+                   B=2, H=16, Lq=8192, Lk=8192, d=64, scale=1.0 / math.sqrt(64), causal=False,
+                   mask="window512_elem_rand10", seed=6),
+}
+
+
+def extension_bitmap_mask():
+    c = EXTENSION_CONFIGS["bitmap"]
+    return window_bitmap_mask(c["seed"], c["Lq"], window=512, frac=0.10)
+
+
 def config_block_mask(cfg: int):
     c = CONFIGS[cfg]
     if c.get("mask") != "window512_rand10":
