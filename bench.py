@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 KERNEL_SOURCES = {
-    "copy": None, "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
+    "copy": None, "bitmap": "attention_bf16.hip", "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip",
 }
 
@@ -148,6 +148,30 @@ def setup_sparse(rf, torch, W):
                 extra={"active_tiles_per_head": int(bm.sum()), "tiles_per_head": int(bm.size)})
 
 
+def setup_bitmap(rf, torch, W):
+    """Extension workload: element bitmaps inside partial tiles (a 512-key
+    element-level causal window plus random tiles), at the block-sparse shape."""
+    c = W.EXTENSION_CONFIGS["bitmap"]
+    seed = c["seed"]
+    q, k, v = (torch.from_numpy(W.normal_tensor(seed, t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
+               .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
+    kinds, bits = W.extension_bitmap_mask()
+    kd = torch.from_numpy(kinds).cuda()
+    bd = torch.from_numpy(bits.view(np.int64)).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
+    active = int((kinds != 0).sum())
+    flops = 4 * 64 * 64 * c["d"] * active * c["B"] * c["H"]   # active 64x64 tiles, counted whole
+    n_full = int((kinds == 1).sum())
+    n_vis_part = int(sum(bin(int(w)).count("1") for w in bits[kinds == 2].ravel()))
+    visible = n_full * 64 * 64 + n_vis_part
+    return dict(fn=lambda: rf.rf_attention_fwd_bitmap(q, k, v, kd, bd, scale=c["scale"], causal=c["causal"], out=o,
+                                                      lse=lse),
+                work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, kd, bd, o, lse), cfg=c,
+                extra={"active_tiles_per_head": active, "partial_tiles_per_head": int((kinds == 2).sum()),
+                       "visible_fraction_of_active": round(visible / (active * 64 * 64), 4)})
+
+
 def setup_decode(rf, torch, W):
     c = W.CONFIGS[4]
     B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
@@ -201,7 +225,7 @@ def setup_copy(rf, torch, W):
                 cfg={"name": "calibration_copy_f32_1GiB", "dtype": "f32"})
 
 
-SETUPS = {"copy": setup_copy, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
+SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
           "attn_f32": setup_attn_f32}
 
 
@@ -239,7 +263,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32")
+    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

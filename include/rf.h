@@ -107,6 +107,31 @@ int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float
                      const uint8_t* block_mask, int dtype, void* stream);
 
 /*
+ * rf_attention_fwd with element-level sparsity inside partial tiles.
+ * Source: STOF page, Méthodologie 1, two-level storage format: outer 64 x 64
+ * tiles are skipped, "full" (every element valid) or "partial", and the valid
+ * elements of a partial tile are held as 64-bit bitmaps.
+ *   tile_kind : device uint8 [ceil(Lq/64), ceil(Lk/64)], shared by all (b, h):
+ *               0 = empty (never loaded), 1 = full, any other value = partial.
+ *   tile_bits : device uint64 [ceil(Lq/64), ceil(Lk/64), 64], 16-byte aligned:
+ *               word r of tile (I, J) holds the visibility of query row
+ *               64 I + r for keys 64 J .. 64 J + 63 (bit j mod 64). Read only
+ *               for partial tiles. (The page groups the same 4096 bits of a
+ *               tile by 8 x 8 blocks; here a tile's words are its rows, since
+ *               one lane owns one query row.)
+ *   Other arguments as rf_attention_fwd.
+ * Visible(i, j) = causal rule AND tile rule AND j < Lk, where the tile rule
+ * is kind == 1, or kind not in {0, 1} and the bit of (i, j) set.
+ * Supported as rf_attention_fwd, and the bitmap array must be below 2^32
+ * bytes (RF_ERR_UNSUPPORTED otherwise).
+ * Errors: as rf_attention_fwd, plus RF_ERR_INVALID_ARG for NULL tile_kind or
+ * tile_bits when work exists, or misaligned tile_bits.
+ */
+int rf_attention_fwd_bitmap(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int Lq, int Lk, int d, float scale, int causal, const uint8_t* tile_kind,
+                            const uint64_t* tile_bits, int dtype, void* stream);
+
+/*
  * Bytes of device workspace that rf_attention_decode_splitkv needs:
  * B*H*num_splits*(d + 1) fp32 values (normalised partial outputs and their
  * LSE), rounded up to 256 bytes. Returns 0 for invalid arguments.
@@ -166,7 +191,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 1
+#define RF_ABI_VERSION 2
 int rf_abi_version(void);
 
 #ifdef __cplusplus

@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "RF_F32", "RF_BF16", "RFError", "load", "library_path",
-    "rf_softmax_rows", "rf_attention_fwd", "rf_attention_decode_splitkv",
+    "rf_softmax_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_decode_splitkv",
     "rf_attention_decode_splitkv_workspace_size", "rf_lse_merge", "rf_abi_version",
 ]
 
@@ -52,6 +52,7 @@ def load():
     sig = {
         "rf_softmax_rows": ([P, P, I64, I64, I, P], I),
         "rf_attention_fwd": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P], I),
+        "rf_attention_fwd_bitmap": ([P, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P], I),
         "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_splitkv": ([P, P, P, P, P, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
@@ -164,6 +165,47 @@ def rf_attention_fwd(q, k, v, scale=None, causal=False, block_mask=None, out=Non
     st = lib.rf_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
                               1 if causal else 0, _ptr(block_mask), _dtype_code(q), _stream(dev))
     _check(st, "rf_attention_fwd")
+    return o, lse
+
+
+def rf_attention_fwd_bitmap(q, k, v, tile_kind, tile_bits, scale=None, causal=False, out=None, lse=None,
+                            want_lse=True):
+    """Attention forward with element bitmaps inside partial tiles.
+
+    tile_kind uint8 [ceil(Lq/64), ceil(Lk/64)] (0 empty, 1 full, other = partial);
+    tile_bits int64 or uint64 [ceil(Lq/64), ceil(Lk/64), 64]: word r of a tile is
+    query row r's visibility of the tile's 64 keys (bit j). Returns (o, lse).
+    """
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    want = (math.ceil(Lq / MASK_TILE), math.ceil(Lk / MASK_TILE))
+    if tile_kind.dtype != torch.uint8 or tuple(tile_kind.shape) != want:
+        raise ValueError(f"tile_kind must be uint8 {want}")
+    if tile_bits.dtype not in (torch.int64, getattr(torch, "uint64", torch.int64)) or \
+            tuple(tile_bits.shape) != want + (MASK_TILE,) or not tile_bits.is_contiguous():
+        raise ValueError(f"tile_bits must be contiguous 64-bit {want + (MASK_TILE,)}")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.shape != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be fp32 [B, H, Lq]")
+    dev = _dev(q, k, v, o, lse, tile_kind, tile_bits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.rf_attention_fwd_bitmap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
+                                     1 if causal else 0, _ptr(tile_kind), _ptr(tile_bits), _dtype_code(q),
+                                     _stream(dev))
+    _check(st, "rf_attention_fwd_bitmap")
     return o, lse
 
 

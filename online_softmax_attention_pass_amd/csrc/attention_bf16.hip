@@ -180,25 +180,39 @@ struct TileWalker {
   int bn;  // keys per tile (divides the 64-key mask tile)
   int base = -64;
   uint64_t wg_bits = 0, wv_bits = 0;
+  // With element bitmaps: tiles this wave's mask row has as partial (a kind
+  // other than 0 and 1), and tiles partial for any row of the workgroup.
+  bool bits = false;
+  uint64_t pv_bits = 0, pg_bits = 0;
 
   __device__ void refill(int b) {
     const int kt = b + int(threadIdx.x & 63);
-    bool any = false, mine = false;
+    bool any = false, mine = false, part = false, anypart = false;
     if (kt < kt_end) {
       const int mc = kt * bn / kMaskTile;
       for (int mr = mr0; mr <= mr1; ++mr) {
-        const bool a = mask[int64_t(mr) * n_mask_cols + mc] != 0;
+        const uint8_t kind = mask[int64_t(mr) * n_mask_cols + mc];
+        const bool a = kind != 0;
+        const bool pa = bits && kind != 0 && kind != 1;
         any |= a;
         mine |= (mr == mr_w) && a;
+        anypart |= pa;
+        part |= (mr == mr_w) && pa;
       }
     }
     wg_bits = __builtin_amdgcn_ballot_w64(any);
     wv_bits = __builtin_amdgcn_ballot_w64(mine);
+    if (bits) {
+      pg_bits = __builtin_amdgcn_ballot_w64(anypart);
+      pv_bits = __builtin_amdgcn_ballot_w64(part);
+    }
     base = b;
   }
   // First tile >= kt that the workgroup must visit (kt_end if none); *mine says
-  // whether this wave's mask row has it.
-  __device__ int next(int kt, bool* mine) {
+  // whether this wave's mask row has it. With bitmaps, *part (bit 0: this
+  // wave's row, bit 1: any row of the workgroup) says whether it is partial.
+  __device__ int next(int kt, bool* mine, int* part = nullptr) {
+    if (part != nullptr) *part = 0;
     if (mask == nullptr) {
       *mine = true;
       return kt < kt_end ? kt : kt_end;
@@ -210,6 +224,7 @@ struct TileWalker {
         kt += int(__builtin_ctzll(rest));
         if (kt >= kt_end) break;
         *mine = (wv_bits >> (kt - base)) & 1;
+        if (part != nullptr) *part = int((pv_bits >> (kt - base)) & 1) | (int((pg_bits >> (kt - base)) & 1) << 1);
         return kt;
       }
       kt = base + 64;
@@ -493,6 +508,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* khead, const uint16_t* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (__attribute__((address_space(3))) void*)(vdst + ins * 512), 16,
                                              base + vv_off[j], 0, 0, 0);
   }
+}
+
+// One wave-wide direct-to-LDS load of 1 KiB of tile row bitmaps into bb
+// (lane i writes bytes 16 i .. 16 i + 15); off is this lane's byte offset.
+__device__ __forceinline__ void dma_bits(const uint64_t* bits, uint32_t bytes, uint64_t* bb, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(bits, bytes);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(bb), 16, off, 0, 0, 0);
 }
 
 // One tensor's share of a tile: this wave's n direct-to-LDS instructions.
@@ -806,12 +828,12 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 // a tile's row maximum exceeds it by more than 2^kRescaleSlack. The rescale
 // of O waits for the P.V product that precedes it in phase B.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int WPE>
+template <int D, int NW, int WPE, bool BITS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
     const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group,
-    int64_t item_base) {
+    int64_t item_base, const uint64_t* __restrict__ tile_bits, uint32_t bits_bytes) {
   constexpr int BN = 64;
   constexpr int BM = 32 * NW;
   constexpr int KCH = D / 8;
@@ -831,6 +853,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   __shared__ __align__(16) uint16_t kb1[BN * D];
   __shared__ __align__(16) uint16_t vb0[BN * D];
   __shared__ __align__(16) uint16_t vb1[BN * D];
+  // Row bitmaps of the workgroup's 128 query rows for the tile in kb0 / kb1
+  // (word 32 w + r belongs to wave w's row r), loaded with that tile's K.
+  __shared__ __align__(16) uint64_t bb0[BITS ? 128 : 2];
+  __shared__ __align__(16) uint64_t bb1[BITS ? 128 : 2];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -870,6 +896,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int kt_end = last_key < 0 ? 0 : int(last_key / BN) + 1;
     TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
                     min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
+    walk.bits = BITS;
 
     uint4 qf[KSTEPS];
     {
@@ -969,9 +996,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // diagonal, sequence end), and the whole tile when the wave's block-mask row
     // skips it or the causal diagonal ends before it. A fully hidden tile then
     // contributes exp(-inf) = 0 everywhere.
-    auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine) {
+    // This lane's row word of a tile's bitmaps (read early: it gates the mask).
+    auto row_word = [&](int part, const uint64_t* bb) -> uint64_t {
+      return (BITS && (part & 1)) ? bb[32 * wave + l32] : ~uint64_t(0);
+    };
+    auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine, int part, uint64_t word) {
       const int k0 = kt * BN;
-      const bool edge = !mine || (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
+      const bool bitmap = BITS && (part & 1);
+      const bool edge =
+          !mine || bitmap || (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
       if (edge) {
         const int lim = mine ? row_lim - k0 - 4 * h : -BN;
 #pragma unroll
@@ -979,6 +1012,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
+        if (bitmap) {
+          // Key 32 mb + 8 (r / 4) + 4 h + r % 4 of the tile is visible iff its
+          // bit in this row's word is set.
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const uint32_t w = uint32_t(word >> (32 * mb)) >> (4 * h);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (((w >> (8 * (r >> 2) + (r & 3))) & 1u) == 0) st[mb][r] = kNegInf;
+          }
+        }
       }
     };
     // Row maximum of a tile; moves the reference when it is exceeded by more than
@@ -1069,8 +1113,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     //   phase B1: P.V keys 0..31    with the exponentials of keys 32..63
     //   phase B2: P.V keys 32..63
     auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
-                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next) {
+                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next, int part_next,
+                    const uint64_t* bb_next) {
       uint32_t pk[MB][8];
+      // d = 64 has registers to spare: read the word before phase A.
+      const uint64_t word_next = D <= 64 ? row_word(part_next, bb_next) : 0;
       float lt0 = 0.f, ltr0 = 0.f, lt1 = 0.f, ltr1 = 0.f;
       {
 #pragma unroll
@@ -1104,7 +1151,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[0][i]));
       asm volatile("" ::"v"(lt0), "v"(ltr0));
       commit_half(s_cur, pk, 0, lt0, ltr0);
-      mask_tile(s_next, kt_next, mine_next);
+      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       {
         const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
         constexpr int NB1 = NPV / 2;
@@ -1126,8 +1173,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // One steady-state step: current tile (scores s_cur, V in vs_cur), next tile
     // (K in ks_next, scores into s_next).
     auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
-                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next) {
+                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next, int part_next,
+                    const uint64_t* bb_next) {
       uint32_t pk[MB][8];
+      // d = 64 has registers to spare: read the word before phase A.
+      const uint64_t word_next = D <= 64 ? row_word(part_next, bb_next) : 0;
       float lt = 0.f, ltr = 0.f;
       // Phase A: score product of the next tile with the exponentials of this
       // one, written as NS chunks of one MFMA plus its share of the vector work
@@ -1182,13 +1232,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       asm volatile("" ::"v"(lt), "v"(ltr));
 #if RF_ATT_SUMGUARD
       commit_tile(s_cur, pk, lt, ltr);
-      mask_tile(s_next, kt_next, mine_next);
+      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       // Phase B: P.V product of this tile.
       pv_mfmas(vs_cur, pk);
 #else
       l_run += lt;
       l_rnd += ltr;
-      mask_tile(s_next, kt_next, mine_next);
+      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       // Phase B: P.V product of this tile with the row maximum of the next one.
       pv_mfmas(vs_cur, pk);
       bool moved = false;
@@ -1225,15 +1275,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     f32x16_t s0[MB], s1[MB];
 
     bool m0 = false, m1 = false, m2 = false;
-    int t0 = walk.next(0, &m0);
+    int p0 = 0, p1 = 0, p2 = 0;
+    // Row bitmaps of tile kt into bb, when some row of the workgroup has it as
+    // partial: one wave issues one 1 KiB direct-to-LDS load (lane i: 16 bytes =
+    // rows 2 (i % 32), +1 of mask row q0 / 64 + i / 32).
+    auto load_bits = [&](uint64_t* bb, int kt, int part) {
+      if (BITS && (part & 2) && wave == 0) {
+        const uint32_t mr = uint32_t(q0 / kMaskTile + (lane >> 5));
+        const uint32_t off = ((mr * uint32_t(n_mask_cols) + uint32_t(kt)) * 64u + 2u * uint32_t(lane & 31)) * 8u;
+        dma_bits(tile_bits, bits_bytes, bb, off);
+      }
+    };
+    int t0 = walk.next(0, &m0, &p0);
     if (t0 < kt_end) {
-      int t1 = walk.next(t0 + 1, &m1);
+      int t1 = walk.next(t0 + 1, &m1, &p1);
       dma_one(khead, head_bytes, kb0, uint32_t(t0) * BN * D * 2, kv_off, wave * IPW, IPW);
       dma_one(vhead, head_bytes, vb0, uint32_t(t0) * BN * D * 2, vv_off, wave * IPW, IPW);
-      if (t1 < kt_end) dma_one(khead, head_bytes, kb1, uint32_t(t1) * BN * D * 2, kv_off, wave * IPW, IPW);
+      load_bits(bb0, t0, p0);
+      if (t1 < kt_end) {
+        dma_one(khead, head_bytes, kb1, uint32_t(t1) * BN * D * 2, kv_off, wave * IPW, IPW);
+        load_bits(bb1, t1, p1);
+      }
       __syncthreads();  // K(t0), K(t1), V(t0) resident
       score_mfmas(kb0, s0);
-      mask_tile(s0, t0, m0);
+      mask_tile(s0, t0, m0, p0, row_word(p0, bb0));
       {
         bool moved = false;
         const float alpha = tile_max(s0, &moved);
@@ -1246,10 +1311,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       while (true) {
         __syncthreads();  // loads of the previous step resident; kb0 and vb1 free
         if (t1 >= kt_end) break;
-        int t2 = walk.next(t1 + 1, &m2);
-        if (t2 < kt_end) dma_one(khead, head_bytes, kb0, uint32_t(t2) * BN * D * 2, kv_off, wave * IPW, IPW);
+        int t2 = walk.next(t1 + 1, &m2, &p2);
+        if (t2 < kt_end) {
+          dma_one(khead, head_bytes, kb0, uint32_t(t2) * BN * D * 2, kv_off, wave * IPW, IPW);
+          load_bits(bb0, t2, p2);
+        }
         dma_one(vhead, head_bytes, vb1, uint32_t(t1) * BN * D * 2, vv_off, wave * IPW, IPW);
-        step(kb1, vb0, s0, s1, t1, m1);
+        step(kb1, vb0, s0, s1, t1, m1, p1, bb1);
 
         __syncthreads();  // kb1 and vb0 free
         if (t2 >= kt_end) {
@@ -1259,12 +1327,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           break;
         }
         bool m3 = false;
-        const int t3 = walk.next(t2 + 1, &m3);
-        if (t3 < kt_end) dma_one(khead, head_bytes, kb1, uint32_t(t3) * BN * D * 2, kv_off, wave * IPW, IPW);
+        int p3 = 0;
+        const int t3 = walk.next(t2 + 1, &m3, &p3);
+        if (t3 < kt_end) {
+          dma_one(khead, head_bytes, kb1, uint32_t(t3) * BN * D * 2, kv_off, wave * IPW, IPW);
+          load_bits(bb1, t3, p3);
+        }
         dma_one(vhead, head_bytes, vb0, uint32_t(t2) * BN * D * 2, vv_off, wave * IPW, IPW);
-        step(kb0, vb1, s1, s0, t2, m2);
+        step(kb0, vb1, s1, s0, t2, m2, p2, bb0);
         t1 = t3;
         m1 = m3;
+        p1 = p3;
       }
       finish(last_in_vb1 ? vb1 : vb0, s0);
     }
@@ -1657,9 +1730,10 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
   return hipGetLastError();
 }
 
-template <int D, int NW, int WPE, int BN, bool SP>
+template <int D, int NW, int WPE, int BN, bool SP, bool BITS = false>
 hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
-                      int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream) {
+                      int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream,
+                      const uint64_t* tile_bits = nullptr) {
   constexpr int BM = 32 * NW;
   const int n_qt = (Lq + BM - 1) / BM;
   const int64_t n_items = int64_t(B) * H * n_qt;
@@ -1675,15 +1749,19 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
   const int64_t cap = 1LL << 22;
   const unsigned grid = unsigned(n_items < cap ? n_items : cap);
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
+  // Bytes of the row-bitmap array (validated below 2^32 at the boundary).
+  const uint32_t bits_bytes =
+      BITS ? uint32_t(int64_t((Lq + kMaskTile - 1) / kMaskTile) * ((Lk + kMaskTile - 1) / kMaskTile) * 512) : 0u;
   if constexpr (SP) {
     // One workgroup per item; more items than one grid allows go in chunks
     // (then without the XCD placement, which assumes the whole item range).
     for (int64_t base = 0; base < n_items; base += cap) {
       const int64_t n = n_items - base < cap ? n_items - base : cap;
-      hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE>), dim3(unsigned(n)), dim3(NW * 64), 0, stream,
+      hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS>), dim3(unsigned(n)), dim3(NW * 64), 0, stream,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                          static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
-                         block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base);
+                         block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base,
+                         tile_bits, bits_bytes);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1699,7 +1777,14 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
 
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
-                                 hipStream_t stream) {
+                                 const uint64_t* tile_bits, hipStream_t stream) {
+  if (tile_bits != nullptr) {  // element bitmaps: the pipelined kernel only
+    if (d == 128)
+      return launch_dma<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, 64, true, true>(q, k, v, o, lse, B, H, Lq, Lk, scale,
+                                                                             causal, block_mask, stream, tile_bits);
+    return launch_dma<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, 64, true, true>(q, k, v, o, lse, B, H, Lq, Lk, scale,
+                                                                        causal, block_mask, stream, tile_bits);
+  }
 #if RF_ATT_DMA
   if (d == 128)
     return launch_dma<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, RF_ATT_SP ? 64 : RF_ATT_BN_D128, bool(RF_ATT_SP)>(

@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
                                                             const float* __restrict__ v, float* __restrict__ o,
                                                             float* __restrict__ lse, int H, int Lq, int Lk, int d,
                                                             float scale_log2, int causal,
-                                                            const uint8_t* __restrict__ block_mask, int n_qt,
+                                                            const uint8_t* __restrict__ block_mask,
+                                                            const uint64_t* __restrict__ tile_bits, int n_qt,
                                                             int64_t n_items) {
   // Rows padded by 4 floats: 16-byte aligned, and the 16 key rows one
   // instruction reads start 4 banks apart.
@@ -73,9 +74,15 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
     for (int kt = 0; kt < n_kt; ++kt) {
       const int k0 = kt * kBN;
       if (causal && k0 > causal_last) break;  // every later tile is masked too
-      if (block_mask != nullptr &&
-          block_mask[int64_t(q0 / kMaskTile) * n_mask_cols + k0 / kMaskTile] == 0)
-        continue;  // the whole tile is masked: skip it, no load
+      const int64_t tile = int64_t(q0 / kMaskTile) * n_mask_cols + k0 / kMaskTile;
+      const uint8_t kind = block_mask != nullptr ? block_mask[tile] : uint8_t(1);
+      if (kind == 0) continue;  // the whole tile is masked: skip it, no load
+      // A partial tile (kind other than 0 and 1, with bitmaps): bit (j mod 64)
+      // of this row's word says whether key j is visible. The 16 rows of a
+      // workgroup lie in one 64-row mask tile.
+      const bool part = tile_bits != nullptr && kind != 1;
+      uint64_t word = ~uint64_t(0);
+      if (part && qi < Lq) word = tile_bits[tile * kMaskTile + (qi % kMaskTile)];
       __syncthreads();
       for (int i = t; i < kBN * DMAX; i += 256) {
         const int c = i / DMAX, e = i % DMAX;
@@ -107,7 +114,8 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int kj = k0 + p + 16 * j;
-        const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= int64_t(qi) + (Lk - Lq));
+        const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= int64_t(qi) + (Lk - Lq)) &&
+                         ((word >> (kj % kMaskTile)) & 1);
         s[j] = vis ? dots[j] * scale_log2 : kNegInf;
         bm = fmaxf(bm, s[j]);
       }
@@ -162,14 +170,14 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
 
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                                 int H, int Lq, int Lk, int d, float scale, int causal,
-                                const uint8_t* block_mask, hipStream_t stream) {
+                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream) {
   const int n_qt = (Lq + kBM - 1) / kBM;
   const int64_t n_items = int64_t(B) * H * n_qt;
   const unsigned grid = unsigned(n_items < (1LL << 20) ? n_items : (1LL << 20));
   const float scale_log2 = float(double(scale) * 1.4426950408889634);
 #define RF_ATT_F32(DM)                                                                                    \
   hipLaunchKernelGGL((attention_f32_kernel<DM>), dim3(grid), dim3(256), 0, stream, q, k, v, o, lse, H, Lq, \
-                     Lk, d, scale_log2, causal, block_mask, n_qt, n_items)
+                     Lk, d, scale_log2, causal, block_mask, tile_bits, n_qt, n_items)
   if (d <= 32)
     RF_ATT_F32(32);
   else if (d <= 64)

@@ -109,50 +109,78 @@ int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtyp
   }
 }
 
-int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
-                     int Lk, int d, float scale, int causal, const uint8_t* block_mask, int dtype, void* stream) {
+namespace {
+// Shared body of the two attention entry points; `name` labels the errors.
+int attention_common(const char* name, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int H, int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
+                     const uint64_t* tile_bits, int dtype, void* stream) {
   try {
-    if (dtype != RF_F32 && dtype != RF_BF16)
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: unknown dtype %d", dtype);
+    if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
     if (B < 0 || H < 0 || Lq < 0 || Lk < 0)
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: negative size (B=%d H=%d Lq=%d Lk=%d)", B, H, Lq, Lk);
-    if (d < 1) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: d = %d < 1", d);
-    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: scale is not finite");
+      return fail(RF_ERR_INVALID_ARG, "%s: negative size (B=%d H=%d Lq=%d Lk=%d)", name, B, H, Lq, Lk);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "%s: d = %d < 1", name, d);
+    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "%s: scale is not finite", name);
     if (dtype == RF_BF16 && d != 64 && d != 128)
-      return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: bf16 supports d in {64, 128}, got %d", d);
-    if (dtype == RF_F32 && d > 128)
-      return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: fp32 supports d <= 128, got %d", d);
+      return fail(RF_ERR_UNSUPPORTED, "%s: bf16 supports d in {64, 128}, got %d", name, d);
+    if (dtype == RF_F32 && d > 128) return fail(RF_ERR_UNSUPPORTED, "%s: fp32 supports d <= 128, got %d", name, d);
     const int es = dtype == RF_F32 ? 4 : 2;
     int64_t nq = 1, nk = 1;
     if (!mul_ok(nq, B) || !mul_ok(nq, H) || !mul_ok(nq, Lq) || !mul_ok(nq, d) || !mul_ok(nq, es) ||
         !mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, es))
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: tensor size overflows int64");
+      return fail(RF_ERR_INVALID_ARG, "%s: tensor size overflows int64", name);
+    if (tile_bits != nullptr) {
+      // 64 words of 8 bytes per 64 x 64 tile; the bf16 kernel addresses the
+      // array with 32-bit offsets.
+      const int64_t bytes = int64_t((Lq + 63) / 64) * ((Lk + 63) / 64) * 512;
+      if (bytes > int64_t(UINT32_MAX))
+        return fail(RF_ERR_UNSUPPORTED, "%s: tile bitmaps of %lld bytes exceed 2^32", name, (long long)bytes);
+    }
     if (int64_t(B) * H * Lq == 0) return ok();
-    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL q or o");
-    if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: NULL k or v");
+    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL q or o", name);
+    if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "%s: NULL k or v", name);
+    if (tile_bits != nullptr && Lk > 0 && block_mask == nullptr)
+      return fail(RF_ERR_INVALID_ARG, "%s: NULL tile_kind", name);
+    if (tile_bits != nullptr && !aligned(tile_bits, 16))
+      return fail(RF_ERR_INVALID_ARG, "%s: tile_bits must be 16-byte aligned", name);
     if (dtype == RF_BF16) {
       if (int64_t(Lk) * d * 2 > INT32_MAX)
-        return fail(RF_ERR_UNSUPPORTED, "rf_attention_fwd: bf16 path needs Lk * d * 2 < 2^31 bytes per head");
+        return fail(RF_ERR_UNSUPPORTED, "%s: bf16 path needs Lk * d * 2 < 2^31 bytes per head", name);
       if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
-        return fail(RF_ERR_UNSUPPORTED,
-                    "rf_attention_fwd: bf16 path needs 16-byte aligned q, k, v and 8-byte aligned o");
+        return fail(RF_ERR_UNSUPPORTED, "%s: bf16 path needs 16-byte aligned q, k, v and 8-byte aligned o", name);
     } else if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(o, 4)) {
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: fp32 tensors must be 4-byte aligned");
+      return fail(RF_ERR_INVALID_ARG, "%s: fp32 tensors must be 4-byte aligned", name);
     }
-    if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd: lse misaligned");
+    if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "%s: lse misaligned", name);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e =
         dtype == RF_BF16
-            ? rf::launch_attention_bf16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, block_mask, s)
+            ? rf::launch_attention_bf16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, block_mask, tile_bits,
+                                        s)
             : rf::launch_attention_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, Lq, Lk,
-                                       d, scale, causal != 0, block_mask, s);
-    return hip_status(e, "rf_attention_fwd");
+                                       d, scale, causal != 0, block_mask, tile_bits, s);
+    return hip_status(e, name);
   } catch (const std::exception& e) {
-    return fail(RF_ERR_HIP, "rf_attention_fwd: %s", e.what());
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
   } catch (...) {
-    return fail(RF_ERR_HIP, "rf_attention_fwd: unknown exception");
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
   }
+}
+}  // namespace
+
+int rf_attention_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                     int Lk, int d, float scale, int causal, const uint8_t* block_mask, int dtype, void* stream) {
+  return attention_common("rf_attention_fwd", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, block_mask,
+                          nullptr, dtype, stream);
+}
+
+int rf_attention_fwd_bitmap(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int Lq, int Lk, int d, float scale, int causal, const uint8_t* tile_kind,
+                            const uint64_t* tile_bits, int dtype, void* stream) {
+  if (int64_t(B) * H * Lq > 0 && Lk > 0 && tile_bits == nullptr)
+    return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd_bitmap: NULL tile_bits");
+  return attention_common("rf_attention_fwd_bitmap", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, tile_kind,
+                          tile_bits, dtype, stream);
 }
 
 size_t rf_attention_decode_splitkv_workspace_size(int B, int H, int d, int num_splits) {

@@ -128,10 +128,13 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, void* 
 hipError_t launch_decode_partials(const void* q, const void* k, const void* v, float* o_parts,
                                   float* lse_parts, int B, int H, int Lk, int d, float scale,
                                   int num_splits, hipStream_t stream);
+// block_mask: NULL (dense) or tile kinds [ceil(Lq/64), ceil(Lk/64)]. tile_bits:
+// NULL (every nonzero kind is a full tile) or uint64 [same tiles, 64] row
+// bitmaps, used where the kind is neither 0 nor 1.
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                                 int B, int H, int Lq, int Lk, int d, float scale, int causal,
-                                const uint8_t* block_mask, hipStream_t stream);
+                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream);
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int H, int Lq, int Lk, int d, float scale, int causal,
-                                 const uint8_t* block_mask, hipStream_t stream);
+                                 const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream);
 }  // namespace rf

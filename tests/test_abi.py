@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 1
+    assert lib.rf_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -109,6 +109,27 @@ def test_attention_validation(lib, kw, code):
     assert att(lib, **kw) == code
     if code != OK:
         assert "rf_attention_fwd" in _msg(lib)
+
+
+def att_bitmap(lib, **kw):
+    a = dict(ATT, kinds=FAKE, bits=FAKE)
+    a.update(kw)
+    return lib.rf_attention_fwd_bitmap(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"],
+                                       a["d"], a["scale"], a["causal"], a["kinds"], a["bits"], a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=NUL), INVALID), (dict(kinds=NUL), INVALID),
+    (dict(bits=P(0x10008)), INVALID),                     # bitmaps must be 16-byte aligned
+    (dict(dtype=5), INVALID), (dict(d=96), UNSUP), (dict(q=NUL), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(Lq=1 << 18, Lk=1 << 18), UNSUP),                # 4096 x 4096 tiles x 512 B > 2^32 bytes
+    (dict(B=0), OK), (dict(B=0, q=NUL, k=NUL, v=NUL, o=NUL, kinds=NUL, bits=NUL), OK),
+    (dict(Lq=0, bits=NUL), OK),
+])
+def test_attention_bitmap_validation(lib, kw, code):
+    assert att_bitmap(lib, **kw) == code
+    if code != OK:
+        assert "rf_attention_fwd_bitmap" in _msg(lib)
 
 
 def test_library_usable_after_error(lib):

@@ -156,3 +156,28 @@ def test_decode_long_keys(rf_gpu):
     e_o = assert_close(host_f64(o), ref_o, 1e-2, "decode long O")
     e_l = assert_close(host_f64(lse), ref_lse[:, :, 0], 1e-3, "decode long LSE")
     _report("decode long keys", e_o, e_l, ref_o)
+
+
+def test_extension_bitmap_full_size(rf_gpu):
+    """Element bitmaps inside partial tiles at B2 H16 L8192 d64 (a 512-key
+    element-level causal window plus random tiles): two heads, rows at tile and
+    window edges, against the oracle."""
+    import torch
+    c = W.EXTENSION_CONFIGS["bitmap"]
+    q, k, v = (W.normal_tensor(c["seed"], t, c["B"], c["H"], c["Lq"], c["d"], "bf16")
+               for t in (W.TID_Q, W.TID_K, W.TID_V))
+    kinds, bits = W.extension_bitmap_mask()
+    note("extension bitmap full size")
+    o, lse = rf_gpu.rf_attention_fwd_bitmap(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(kinds).cuda(),
+                                            torch.from_numpy(bits.view(np.int64)).cuda(), scale=c["scale"],
+                                            causal=c["causal"])
+    got_o, got_l = host_f64(o), host_f64(lse)
+    rows = [0, 1, 63, 64, 511, 512, 513, 4095, 4096, 8000, 8191]
+    e_o = e_l = 0.0
+    for b, h in ((0, 0), (1, 15)):
+        ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a[b:b + 1, h:h + 1]) for a in (q, k, v)), c["scale"],
+                                     c["causal"], kinds, q_rows=rows, tile_bits=bits)
+        e_o = max(e_o, assert_close(got_o[b:b + 1, h:h + 1, rows], ref_o, 1e-2, "bitmap O"))
+        e_l = max(e_l, assert_close(got_l[b:b + 1, h:h + 1, rows], ref_lse, 1e-3, "bitmap LSE"))
+    assert np.all(np.isfinite(got_l))
+    _report("extension bitmap", e_o, e_l)

@@ -33,8 +33,9 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<MulFunctor<float> > >(int)"
     names = {
         "softmax": "void rf::softmax_rows_reg<float, 4, 512, 16>(float const*)",
-        "prefill": "void rf::attention_bf16_sp_kernel<128, 4, 2>(unsigned short const*)",
-        "sparse": "void rf::attention_bf16_sp_kernel<64, 2, 2>(unsigned short const*)",
+        "prefill": "void rf::attention_bf16_sp_kernel<128, 4, 2, false>(unsigned short const*)",
+        "sparse": "void rf::attention_bf16_sp_kernel<64, 2, 2, false>(unsigned short const*)",
+        "bitmap": "void rf::attention_bf16_sp_kernel<64, 2, 2, true>(unsigned short const*)",
         "decode": "void rf::decode_partial_kernel<128, 8>(unsigned short const*)",
         "attn_f32": "void rf::attention_f32_kernel<64>(float const*)",
     }
@@ -52,7 +53,8 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     assert t["softmax"]["fetch_bytes"] == 1000 * 2048
     assert t["prefill"]["fetch_bytes"] == 2500 * 2048
     assert t["prefill"]["write_bytes"] == 20 * 1024
-    assert t["decode"]["bytes_per_launch"] == 4000 * 2048 + 40 * 1024
+    assert t["decode"]["bytes_per_launch"] == 5000 * 2048 + 50 * 1024
+    assert t["bitmap"]["fetch_bytes"] == 4000 * 2048
     assert t["prefill"]["source_sha"] == traffic.source_sha("attention_bf16.hip")
 
 

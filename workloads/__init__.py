@@ -197,7 +197,7 @@ def window_bitmap_mask(seed: int, L: int, window: int = 512, frac: float = 0.10)
 # partial tiles (the STOF two-level format), at the block-sparse shape.
 EXTENSION_CONFIGS = {
     "bitmap": dict(name="bitmap_sparse_bf16_B2_H16_L8192_d64", kind="attention", dtype="bf16",
-                   B=2, H=16, Lq=8192, Lk=8192, d=64, scale=1.0 / math.sqrt(64), causal=False,
+                   B=2, H=16, Lq=8192, Lk=8192, d=64, scale=1.0 / math.sqrt(64), causal=True,
                    mask="window512_elem_rand10", seed=6),
 }
 
