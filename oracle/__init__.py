@@ -11,6 +11,7 @@ from .oracle import (  # noqa: F401
     bf16_bits_to_f64,
     decode_splitkv_partials,
     element_mask,
+    layernorm_rows,
     logsumexp_rows,
     lse_merge,
     online_attention,

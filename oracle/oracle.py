@@ -22,6 +22,9 @@ Sources (the pages are web summaries of three papers):
   changes, via e^{x-y} = e^x / e^y.
 * STOF page (French), Résumé technique: causal / sliding-window / random
   block masks, with masked tiles skipped instead of computed and reset.
+* RedFuser page, 1. Problématique: normalisation layers are cascaded
+  reductions too (the mean, then the squared deviations from it); the Korean
+  page reports variance as one of its workloads.
 
 Readings where the pages are silent (each also listed in the design notes):
 
@@ -104,6 +107,39 @@ def logsumexp_rows(x: np.ndarray) -> np.ndarray:
         safe = np.where(np.isfinite(m), m, 0.0)
         l = np.sum(np.exp(x - safe[..., None]), axis=-1)
         return np.where(np.isfinite(m), safe + np.log(l), m)
+
+
+# ---------------------------------------------------------------------------
+# layer normalisation of rows: a cascade of two reductions, then a normalise
+# ---------------------------------------------------------------------------
+
+def layernorm_rows(x: np.ndarray, gamma=None, beta=None, eps: float = 1e-5):
+    """Row-wise layer normalisation in fp64, three passes.
+
+    RedFuser page, 1. Problématique (normalisation layers are cascaded
+    reductions) and the Korean page's results (variance as a workload): the
+    mean is one reduction, the sum of squared deviations from it a second
+    that depends on the first, and the output a normalisation by both.
+
+      pass 1: mean_r = (1/n) sum_j x_rj
+      pass 2: var_r  = (1/n) sum_j (x_rj - mean_r)^2       (population variance)
+      pass 3: y_rj   = (x_rj - mean_r) / sqrt(var_r + eps) * gamma_j + beta_j
+
+    gamma, beta: [cols] or None (1 and 0). Returns (y, mean, rstd) with
+    rstd_r = 1 / sqrt(var_r + eps).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    mean = x.sum(axis=-1) / n                                   # pass 1
+    dev = x - mean[..., None]
+    var = (dev * dev).sum(axis=-1) / n                          # pass 2
+    rstd = 1.0 / np.sqrt(var + eps)
+    y = dev * rstd[..., None]                                   # pass 3
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=np.float64)
+    if beta is not None:
+        y = y + np.asarray(beta, dtype=np.float64)
+    return y, mean, rstd
 
 
 # ---------------------------------------------------------------------------

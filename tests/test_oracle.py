@@ -698,3 +698,104 @@ def test_bitmap_workload_mask():
         got = set(np.nonzero(vr)[0].tolist())
         assert window <= got
         assert all(kinds[i // 64, j // 64] == 1 and j // 64 <= i // 64 - wt - 1 for j in got - window)
+
+
+# ---------------------------------------------------------------------------
+# layer normalisation rows (the mean / variance cascade)
+# ---------------------------------------------------------------------------
+
+def pin_ln_bruteforce(ln):
+    r = np.random.default_rng(31)
+    x = r.normal(2, 3, size=(5, 37))
+    g, b = r.normal(1, 0.2, 37), r.normal(0, 0.3, 37)
+    y, mean, rstd = ln(x, g, b, 1e-3)
+    for i in range(5):
+        row = [float(t) for t in x[i]]
+        m = math.fsum(row) / 37
+        v = math.fsum((t - m) ** 2 for t in row) / 37
+        rs = 1 / math.sqrt(v + 1e-3)
+        if abs(mean[i] - m) > 1e-13 or abs(rstd[i] - rs) > 1e-12 * rs:
+            return False
+        if max(abs(y[i, j] - ((row[j] - m) * rs * g[j] + b[j])) for j in range(37)) > 1e-12:
+            return False
+    return True
+
+
+def pin_ln_closed_forms(ln):
+    # two elements a, b: mean (a+b)/2, variance ((a-b)/2)^2, outputs +-(a-b)/2 * rstd
+    y, mean, rstd = ln(np.array([[3.0, -1.0]]), None, None, 0.0)
+    if abs(mean[0] - 1.0) > 1e-15 or abs(rstd[0] - 0.5) > 1e-15 or np.max(np.abs(y - [[1.0, -1.0]])) > 1e-15:
+        return False
+    # a constant row has zero variance: y = beta exactly, rstd = 1/sqrt(eps)
+    beta = np.arange(6.0)
+    y, mean, rstd = ln(np.full((1, 6), 7.25), np.full(6, 3.0), beta, 0.25)
+    return bool(mean[0] == 7.25 and rstd[0] == 2.0 and np.array_equal(y[0], beta))
+
+
+def pin_ln_invariances(ln):
+    r = np.random.default_rng(32)
+    x = r.normal(0, 1.5, size=(8, 300))
+    y0, _, _ = ln(x, None, None, 0.0)
+    for c in (1000.0, -1000.0, 50.0):                       # shift invariance
+        if np.max(np.abs(ln(x + c, None, None, 0.0)[0] - y0)) > 1e-9:
+            return False
+    if np.max(np.abs(ln(4.0 * x, None, None, 0.0)[0] - y0)) > 1e-12:   # scale invariance (eps = 0)
+        return False
+    # normalised rows: mean 0, mean square var / (var + eps)
+    y, _, rstd = ln(x, None, None, 0.5)
+    var = x.var(axis=1)
+    return bool(np.max(np.abs(y.mean(1))) < 1e-13 and
+                np.max(np.abs((y * y).mean(1) - var / (var + 0.5))) < 1e-12)
+
+
+def pin_ln_numpy(ln):
+    r = np.random.default_rng(33)
+    x = r.normal(-3, 2, size=(6, 1000))
+    g, b = r.normal(1, 0.1, 1000), r.normal(0, 0.1, 1000)
+    y, mean, rstd = ln(x, g, b, 1e-5)
+    want = (x - x.mean(1, keepdims=True)) / np.sqrt(x.var(1, keepdims=True) + 1e-5) * g + b
+    return bool(np.max(np.abs(y - want)) < 1e-12 and np.max(np.abs(mean - x.mean(1))) < 1e-13)
+
+
+def test_layernorm_pins():
+    assert pin_ln_bruteforce(O.layernorm_rows)
+    assert pin_ln_closed_forms(O.layernorm_rows)
+    assert pin_ln_invariances(O.layernorm_rows)
+    assert pin_ln_numpy(O.layernorm_rows)
+
+
+def _ln_mutant(kind):
+    def fn(x, gamma=None, beta=None, eps=1e-5):
+        x = np.asarray(x, np.float64)
+        n = x.shape[-1]
+        mean = x.sum(-1) / n
+        dev = x - mean[..., None]
+        var = (dev * dev).sum(-1) / (n - 1 if kind == "sample_variance" and n > 1 else n)
+        if kind == "eps_outside_sqrt":
+            rstd = 1.0 / (np.sqrt(var) + eps)
+        elif kind == "no_sqrt":
+            rstd = 1.0 / (var + eps)
+        else:
+            rstd = 1.0 / np.sqrt(var + eps)
+        y = (x if kind == "no_centering" else dev) * rstd[..., None]
+        g = None if gamma is None else np.asarray(gamma, np.float64)
+        b = None if beta is None else np.asarray(beta, np.float64)
+        if kind == "gamma_beta_swapped":
+            g, b = b, g
+        if g is not None:
+            y = y * g
+        if b is not None:
+            y = y + b
+        return y, mean, rstd
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["sample_variance", "eps_outside_sqrt", "no_sqrt", "no_centering",
+                                  "gamma_beta_swapped"])
+def test_layernorm_mutants_are_caught(kind):
+    fn = _ln_mutant(kind)
+    with np.errstate(all="ignore"):
+        ok = pin_ln_bruteforce(fn) and pin_ln_closed_forms(fn) and pin_ln_invariances(fn) and pin_ln_numpy(fn)
+    assert not ok
+    none = _ln_mutant("none")
+    assert pin_ln_bruteforce(none) and pin_ln_closed_forms(none) and pin_ln_invariances(none) and pin_ln_numpy(none)

@@ -28,6 +28,7 @@ import numpy as np
 
 # Tensor ids inside one config's seed space.
 TID_Q, TID_K, TID_V, TID_X, TID_MASK, TID_U = 0, 1, 2, 3, 4, 5
+TID_GAMMA, TID_BETA = 6, 7
 
 MASK_TILE = 64  # granularity of the block mask, in tokens, on both axes
 
@@ -199,7 +200,18 @@ EXTENSION_CONFIGS = {
     "bitmap": dict(name="bitmap_sparse_bf16_B2_H16_L8192_d64", kind="attention", dtype="bf16",
                    B=2, H=16, Lq=8192, Lk=8192, d=64, scale=1.0 / math.sqrt(64), causal=True,
                    mask="window512_elem_rand10", seed=6),
+    # Row layer normalisation (mean and variance as one fused reduction), at the
+    # softmax workload's shape; rows are drawn as the softmax rows are.
+    "layernorm": dict(name="layernorm_f32_4096x32768", kind="layernorm", dtype="f32", rows=4096, cols=32768,
+                      eps=1e-5, seed=7),
 }
+
+
+def layernorm_affine(seed: int, cols: int):
+    """gamma ~ 1 + 0.1 N(0, 1) and beta ~ 0.1 N(0, 1), float32 [cols]."""
+    g = (1.0 + 0.1 * rng(seed, TID_GAMMA).standard_normal(cols)).astype(np.float32)
+    b = (0.1 * rng(seed, TID_BETA).standard_normal(cols)).astype(np.float32)
+    return g, b
 
 
 def extension_bitmap_mask():
