@@ -40,7 +40,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 KERNEL_SOURCES = {
-    "copy": None, "bitmap": "attention_bf16.hip", "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
+    "copy": None, "bitmap": "attention_bf16.hip", "layernorm": "layernorm_rows.hip", "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip",
 }
 
@@ -148,6 +148,29 @@ def setup_sparse(rf, torch, W):
                 extra={"active_tiles_per_head": int(bm.sum()), "tiles_per_head": int(bm.size)})
 
 
+def setup_layernorm(rf, torch, W):
+    """Extension workload: row layer normalisation of fp32 4096 x 32768 (the
+    softmax shape), two alternating buffer sets like the softmax workload."""
+    c = W.EXTENSION_CONFIGS["layernorm"]
+    x = W.softmax_rows_input(c["seed"], c["rows"], c["cols"])
+    g, b = W.layernorm_affine(c["seed"], c["cols"])
+    gd, bd = torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda()
+    sets = []
+    for _ in range(2):
+        xd = torch.from_numpy(x).cuda()
+        sets.append((xd, torch.empty_like(xd), torch.empty(c["rows"], device="cuda"),
+                     torch.empty(c["rows"], device="cuda")))
+    turn = [0]
+
+    def call():
+        xd, yd, md, rd = sets[turn[0]]
+        turn[0] ^= 1
+        rf.rf_layernorm_rows(xd, gd, bd, eps=c["eps"], out=yd, mean=md, rstd=rd)
+    nbytes = 2 * x.size * 4 + 2 * c["cols"] * 4 + 2 * c["rows"] * 4   # x, y, gamma, beta, mean, rstd
+    return dict(fn=call, work=nbytes, unit="GB/s", bound="hbm", keep=(sets, gd, bd), cfg=c,
+                extra={"buffer_sets": 2})
+
+
 def setup_bitmap(rf, torch, W):
     """Extension workload: element bitmaps inside partial tiles (a 512-key
     element-level causal window plus random tiles), at the block-sparse shape."""
@@ -225,7 +248,7 @@ def setup_copy(rf, torch, W):
                 cfg={"name": "calibration_copy_f32_1GiB", "dtype": "f32"})
 
 
-SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
+SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
           "attn_f32": setup_attn_f32}
 
 
@@ -263,7 +286,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap")
+    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -78,6 +78,29 @@ typedef enum {
 int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype, void* stream);
 
 /*
+ * Row-wise layer normalisation: per row r, with n = cols,
+ *   mean_r = (1/n) sum_j x_rj,  var_r = (1/n) sum_j (x_rj - mean_r)^2,
+ *   y_rj   = (x_rj - mean_r) / sqrt(var_r + eps) * gamma_j + beta_j.
+ * Source: RedFuser page, 1. Problématique (normalisation layers are cascaded
+ * reductions: the mean, then the squared deviations from it) and 2.
+ * Méthodologie (the chain fused into one reduction tree, input read once);
+ * the Korean page reports variance as a workload.
+ *   x, y   : [rows, cols] of `dtype` (RF_F32 or RF_BF16), device pointers.
+ *   gamma, beta : fp32 [cols] or NULL (1 and 0).
+ *   mean, rstd  : fp32 [rows] or NULL; written with mean_r and 1/sqrt(var_r + eps).
+ *   eps    : finite, >= 0 (eps = 0 and a constant row give NaN, as the
+ *            definition does).
+ * Each element is read once and written once when the row fits in registers
+ * (cols <= 32768 with 16-byte aligned rows, gamma and beta and cols a
+ * multiple of 4 (fp32) or 8 (bf16); cols <= 16384 otherwise); longer rows
+ * take a second read.
+ * Errors: RF_ERR_INVALID_ARG (NULL x or y with rows > 0, rows < 0, cols < 1,
+ * bad eps, overflow, misalignment, unknown dtype).
+ */
+int rf_layernorm_rows(const void* x, const float* gamma, const float* beta, void* y, float* mean, float* rstd,
+                      int64_t rows, int64_t cols, float eps, int dtype, void* stream);
+
+/*
  * Attention forward with the online softmax, single-segment strategy (one
  * workgroup sweeps every visible key tile of its query tile).
  * Source: RedFuser page, 1. Problématique (safe softmax then GEMM) and

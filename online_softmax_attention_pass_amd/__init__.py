@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "RF_F32", "RF_BF16", "RFError", "load", "library_path",
-    "rf_softmax_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_decode_splitkv",
+    "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_decode_splitkv",
     "rf_attention_decode_splitkv_workspace_size", "rf_lse_merge", "rf_abi_version",
 ]
 
@@ -51,6 +51,7 @@ def load():
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "rf_softmax_rows": ([P, P, I64, I64, I, P], I),
+        "rf_layernorm_rows": ([P, P, P, P, P, P, I64, I64, F, I, P], I),
         "rf_attention_fwd": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P], I),
         "rf_attention_fwd_bitmap": ([P, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P], I),
         "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
@@ -131,6 +132,35 @@ def rf_softmax_rows(x, out=None):
     rows = x.numel() // cols
     _check(lib.rf_softmax_rows(_ptr(x), _ptr(y), rows, cols, _dtype_code(x), _stream(dev)), "rf_softmax_rows")
     return y
+
+
+def rf_layernorm_rows(x, gamma=None, beta=None, eps=1e-5, out=None, mean=None, rstd=None, want_stats=True):
+    """Row layer normalisation of x [rows, cols] (fp32 or bf16); gamma, beta fp32 [cols] or None.
+
+    Returns (y, mean, rstd): y like x; mean and rstd fp32 [rows] (None if want_stats is False).
+    """
+    torch = _torch()
+    lib = load()
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [rows, cols] tensor")
+    rows, cols = x.shape
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (cols,) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous fp32 [{cols}]")
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("out must match x")
+    if want_stats:
+        mean = torch.empty(rows, dtype=torch.float32, device=x.device) if mean is None else mean
+        rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if rstd is None else rstd
+    for name, t in (("mean", mean), ("rstd", rstd)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (rows,)):
+            raise ValueError(f"{name} must be fp32 [{rows}]")
+    dev = _dev(x, gamma, beta, y, mean, rstd)
+    st = lib.rf_layernorm_rows(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, cols,
+                               float(eps), _dtype_code(x), _stream(dev))
+    _check(st, "rf_layernorm_rows")
+    return y, mean, rstd
 
 
 def rf_attention_fwd(q, k, v, scale=None, causal=False, block_mask=None, out=None, lse=None, want_lse=True):

@@ -23,6 +23,7 @@ ARCH = "gfx950"
 SOURCES = [
     "rf_api.cpp",
     "softmax_rows.hip",
+    "layernorm_rows.hip",
     "lse_merge.hip",
     "decode_splitkv.hip",
     "attention_f32.hip",

@@ -109,6 +109,34 @@ int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtyp
   }
 }
 
+int rf_layernorm_rows(const void* x, const float* gamma, const float* beta, void* y, float* mean, float* rstd,
+                      int64_t rows, int64_t cols, float eps, int dtype, void* stream) {
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16)
+      return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: unknown dtype %d", dtype);
+    if (rows < 0) return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: rows < 0");
+    if (cols < 1) return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: cols < 1");
+    if (!std::isfinite(eps) || eps < 0.f) return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: eps must be finite and >= 0");
+    int64_t n = 1;
+    if (!mul_ok(n, rows) || !mul_ok(n, cols) || !mul_ok(n, 4))
+      return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: rows * cols overflows int64");
+    if (rows == 0) return ok();
+    if (x == nullptr || y == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: NULL x or y");
+    const size_t es = dtype == RF_F32 ? 4 : 2;
+    if (!aligned(x, es) || !aligned(y, es) || (gamma != nullptr && !aligned(gamma, 4)) ||
+        (beta != nullptr && !aligned(beta, 4)) || (mean != nullptr && !aligned(mean, 4)) ||
+        (rstd != nullptr && !aligned(rstd, 4)))
+      return fail(RF_ERR_INVALID_ARG, "rf_layernorm_rows: misaligned pointer");
+    return hip_status(rf::launch_layernorm_rows(x, gamma, beta, y, mean, rstd, rows, cols, eps, dtype,
+                                                static_cast<hipStream_t>(stream)),
+                      "rf_layernorm_rows");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "rf_layernorm_rows: %s", e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "rf_layernorm_rows: unknown exception");
+  }
+}
+
 namespace {
 // Shared body of the two attention entry points; `name` labels the errors.
 int attention_common(const char* name, const void* q, const void* k, const void* v, void* o, float* lse, int B,

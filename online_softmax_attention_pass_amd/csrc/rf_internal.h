@@ -123,6 +123,8 @@ __device__ __forceinline__ void ml_combine_nat(float& m, float& l, float m2, flo
 namespace rf {
 hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype,
                                hipStream_t stream);
+hipError_t launch_layernorm_rows(const void* x, const float* gamma, const float* beta, void* y, float* mean,
+                                 float* rstd, int64_t rows, int64_t cols, float eps, int dtype, hipStream_t stream);
 hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse,
                             int64_t n_rows, int num_splits, int d, int out_dtype, hipStream_t stream);
 hipError_t launch_decode_partials(const void* q, const void* k, const void* v, float* o_parts,

@@ -14,45 +14,10 @@
 #include <stdint.h>
 
 #include "rf_internal.h"
+#include "rows_io.h"
 
 namespace rf {
 namespace {
-
-// Element access: fp32 or bf16 (raw bits), as 16-byte vectors of EPV elements
-// or single elements (EPV = 1) when the row is not 16-byte aligned.
-template <typename T, int EPV> struct Io;
-
-template <> struct Io<float, 4> {
-  __device__ static void load(const float* p, float (&o)[4]) {
-    const float4 v = nt_load(reinterpret_cast<const float4*>(p));
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-  }
-  __device__ static void store(float* p, const float (&o)[4]) {
-    float4 v = make_float4(o[0], o[1], o[2], o[3]);
-    nt_store(v, reinterpret_cast<float4*>(p));
-  }
-};
-template <> struct Io<float, 1> {
-  __device__ static void load(const float* p, float (&o)[1]) { o[0] = *p; }
-  __device__ static void store(float* p, const float (&o)[1]) { *p = o[0]; }
-};
-template <> struct Io<uint16_t, 8> {
-  __device__ static void load(const uint16_t* p, float (&o)[8]) {
-    const uint4 v = nt_load(reinterpret_cast<const uint4*>(p));
-    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-    o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
-  }
-  __device__ static void store(uint16_t* p, const float (&o)[8]) {
-    uint4 v;
-    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
-    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
-    nt_store(v, reinterpret_cast<uint4*>(p));
-  }
-};
-template <> struct Io<uint16_t, 1> {
-  __device__ static void load(const uint16_t* p, float (&o)[1]) { o[0] = bf16_to_f32(*p); }
-  __device__ static void store(uint16_t* p, const float (&o)[1]) { *p = uint16_t(f32_to_bf16_bits(o[0])); }
-};
 
 // Workgroup-wide (+)-reduction of (m, l): wavefront butterfly, then LDS across waves.
 template <int BLOCK>

@@ -28,6 +28,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # (substring of the kernel name, workload, kernel source)
 KERNELS = [
     ("softmax_rows", "softmax", "softmax_rows.hip"),
+    ("layernorm_rows", "layernorm", "layernorm_rows.hip"),
     ("attention_bf16_sp_kernel<128, 4, 2, false>", "prefill", "attention_bf16.hip"),
     ("attention_bf16_sp_kernel<64, 2, 2, false>", "sparse", "attention_bf16.hip"),
     ("attention_bf16_sp_kernel<64, 2, 2, true>", "bitmap", "attention_bf16.hip"),

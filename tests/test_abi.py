@@ -79,6 +79,25 @@ def test_softmax_validation(lib, args, code):
     assert (_msg(lib) == "") == (code == OK)
 
 
+@pytest.mark.parametrize("args,code", [
+    ((NUL, NUL, NUL, NUL, NUL, NUL, 4, 8, 1e-5, F32), INVALID),        # NULL x, y with work
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, -1, 8, 1e-5, F32), INVALID),     # rows < 0
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, 4, 0, 1e-5, F32), INVALID),      # cols < 1
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, 4, 8, -1.0, F32), INVALID),      # eps < 0
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, 4, 8, float("nan"), F32), INVALID),
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, 4, 8, 1e-5, 9), INVALID),        # dtype
+    ((FAKE, NUL, NUL, FAKE, NUL, NUL, 1 << 40, 1 << 40, 1e-5, F32), INVALID),
+    ((FAKE, P(0x10002), NUL, FAKE, NUL, NUL, 4, 8, 1e-5, F32), INVALID),   # misaligned gamma
+    ((P(0x10001), NUL, NUL, FAKE, NUL, NUL, 4, 8, 1e-5, BF16), INVALID),   # misaligned bf16 x
+    ((NUL, NUL, NUL, NUL, NUL, NUL, 0, 8, 1e-5, F32), OK),             # no rows
+])
+def test_layernorm_validation(lib, args, code):
+    assert lib.rf_layernorm_rows(*args, NUL) == code
+    assert (_msg(lib) == "") == (code == OK)
+    if code != OK:
+        assert "rf_layernorm_rows" in _msg(lib)
+
+
 ATT = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=3, Lq=100, Lk=90, d=128, scale=0.1, causal=1,
            mask=NUL, dtype=BF16)
 

@@ -181,3 +181,23 @@ def test_extension_bitmap_full_size(rf_gpu):
         e_l = max(e_l, assert_close(got_l[b:b + 1, h:h + 1, rows], ref_lse, 1e-3, "bitmap LSE"))
     assert np.all(np.isfinite(got_l))
     _report("extension bitmap", e_o, e_l)
+
+
+def test_extension_layernorm_full_size(rf_gpu):
+    """Layer normalisation of fp32 4096 x 32768 (the softmax workload's shape):
+    sampled rows against the oracle, every row's statistics cheaply."""
+    import torch
+    c = W.EXTENSION_CONFIGS["layernorm"]
+    x = W.softmax_rows_input(c["seed"], c["rows"], c["cols"])
+    g, b = W.layernorm_affine(c["seed"], c["cols"])
+    note("extension layernorm full size")
+    y, mean, rstd = rf_gpu.rf_layernorm_rows(dev_f32(x), torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(),
+                                             eps=c["eps"])
+    rows = [0, 1, 2047, 4095]
+    ry, rm, rr = O.layernorm_rows(x[rows].astype(np.float64), g, b, c["eps"])
+    e = assert_close(host_f64(y)[rows], ry, 1e-5, "layernorm y")
+    # all rows: the statistics against the oracle's
+    _, rm_all, rr_all = O.layernorm_rows(x.astype(np.float64), None, None, c["eps"])
+    assert np.all(np.abs(host_f64(mean) - rm_all) <= 1e-6 * np.abs(rm_all) + 1e-6)
+    assert np.all(np.abs(host_f64(rstd) - rr_all) <= 1e-6 * np.abs(rr_all) + 1e-6)
+    _report("extension layernorm", e, 0.0)

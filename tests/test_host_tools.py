@@ -33,6 +33,7 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<MulFunctor<float> > >(int)"
     names = {
         "softmax": "void rf::softmax_rows_reg<float, 4, 512, 16>(float const*)",
+        "layernorm": "void rf::layernorm_rows_reg<float, 4, 512, 16>(float const*)",
         "prefill": "void rf::attention_bf16_sp_kernel<128, 4, 2, false>(unsigned short const*)",
         "sparse": "void rf::attention_bf16_sp_kernel<64, 2, 2, false>(unsigned short const*)",
         "bitmap": "void rf::attention_bf16_sp_kernel<64, 2, 2, true>(unsigned short const*)",
@@ -41,7 +42,7 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     }
     # the fetch counter reads half of the copy's 1 GiB, the write counter all of it
     fetch = [(copy, 524288.0), (copy, 524288.0)] + [(n, 1000.0 * (i + 1)) for i, n in enumerate(names.values())]
-    fetch += [(names["prefill"], 3000.0)]                         # second dispatch: mean is 2500
+    fetch += [(names["prefill"], 5000.0)]                         # second dispatch: mean is 4000
     write = [(copy, 1048576.0)] + [(n, 10.0 * (i + 1)) for i, n in enumerate(names.values())]
     fcsv, wcsv, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
     _write_counters(fcsv, "FETCH_SIZE", fetch)
@@ -51,10 +52,11 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     assert t["calibration"]["fetch_bytes_per_kib"] == pytest.approx(2048.0)
     assert t["calibration"]["write_bytes_per_kib"] == pytest.approx(1024.0)
     assert t["softmax"]["fetch_bytes"] == 1000 * 2048
-    assert t["prefill"]["fetch_bytes"] == 2500 * 2048
-    assert t["prefill"]["write_bytes"] == 20 * 1024
-    assert t["decode"]["bytes_per_launch"] == 5000 * 2048 + 50 * 1024
-    assert t["bitmap"]["fetch_bytes"] == 4000 * 2048
+    assert t["prefill"]["fetch_bytes"] == 4000 * 2048          # (3000 + 5000) / 2
+    assert t["prefill"]["write_bytes"] == 30 * 1024
+    assert t["decode"]["bytes_per_launch"] == 6000 * 2048 + 60 * 1024
+    assert t["bitmap"]["fetch_bytes"] == 5000 * 2048
+    assert t["layernorm"]["write_bytes"] == 20 * 1024
     assert t["prefill"]["source_sha"] == traffic.source_sha("attention_bf16.hip")
 
 
