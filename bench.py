@@ -23,7 +23,6 @@ workload, on this host's cores, and scales it to the same unit.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -40,16 +39,15 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 
 KERNEL_SOURCES = {
-    "copy": None, "bitmap": "attention_bf16.hip", "layernorm": "layernorm_rows.hip", "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
-    "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip",
+    "copy": None, "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
+    "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip", "bitmap": "attention_bf16.hip",
+    "layernorm": "layernorm_rows.hip",
 }
 
 
 def source_sha(name: str) -> str:
-    p = os.path.join(ROOT, "online_softmax_attention_pass_amd", "csrc", name)
-    h = hashlib.sha256(open(p, "rb").read())
-    h.update(open(os.path.join(ROOT, "online_softmax_attention_pass_amd", "csrc", "rf_internal.h"), "rb").read())
-    return h.hexdigest()[:16]
+    from online_softmax_attention_pass_amd.traffic import source_sha as sha
+    return sha(name, os.path.join(ROOT, "online_softmax_attention_pass_amd", "csrc"))
 
 
 def measured_traffic(workload: str):

@@ -11,7 +11,7 @@ kernel over 1 GiB fp32: 2^30 bytes read and 2^30 bytes written per dispatch),
 so the figures are HBM bytes in the units the copy defines.
 
 The output maps each workload to its kernel's bytes per launch together with
-the sha256 of the kernel source it was measured on; bench.py reports the
+the sha256 of the kernel source (and the headers it includes) it was measured on; bench.py reports the
 figure only while that source is unchanged.
 """
 from __future__ import annotations
@@ -20,6 +20,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -39,9 +40,22 @@ COPY_KEY = "MulFunctor"
 COPY_BYTES = float(1 << 30)
 
 
-def source_sha(name: str) -> str:
-    h = hashlib.sha256(open(os.path.join(CSRC, name), "rb").read())
-    h.update(open(os.path.join(CSRC, "rf_internal.h"), "rb").read())
+def source_sha(name: str, csrc: str = CSRC) -> str:
+    """sha256[:16] over a kernel source and, in include order, every local
+    header it pulls in (``#include "..."``, followed recursively)."""
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(fname):
+        if fname in seen:
+            return
+        seen.add(fname)
+        text = open(os.path.join(csrc, fname), "rb").read()
+        h.update(text)
+        for inc in re.findall(rb'^#include "([^"]+)"', text, re.M):
+            add(inc.decode())
+
+    add(name)
     return h.hexdigest()[:16]
 
 
