@@ -219,6 +219,41 @@ def attention(q, k, v, scale: float, causal: bool = False, block_mask=None,
     return O, LSE
 
 
+def decode_gqa(q, k, v, scale: float):
+    """Decode with grouped queries, in fp64: one token per query head, and
+    query heads that share key/value heads (RedFuser page, 4. Résultats
+    Expérimentaux: the MHA and MLA workloads).
+
+    q: [B, Hq, d]; k, v: [B, Hkv, Lk, d] with Hq = G * Hkv. Query head hq reads
+    key/value head hq // G (G consecutive query heads per key/value head; Hkv = 1
+    is the MLA sharing pattern). Per query head, unmasked:
+      s_j = scale * (q . k_j);  m = max_j s_j;  l = sum_j exp(s_j - m);
+      o = sum_j exp(s_j - m) v_j / l;  lse = m + ln l.
+    Lk = 0 gives o = 0 and lse = -inf. Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    assert Hq % Hkv == 0
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, v.shape[3]))
+    lse = np.full((B, Hq), NEG_INF)
+    if Lk == 0:
+        return o, lse
+    for b in range(B):
+        for hq in range(Hq):
+            kh, vh = k[b, hq // G], v[b, hq // G]
+            s_ = scale * (kh @ q[b, hq])                  # scores, one per key
+            m = s_.max()                                   # pass 1
+            e = np.exp(s_ - m)
+            l = e.sum()                                    # pass 2
+            o[b, hq] = (e @ vh) / l                        # pass 3 and the P.V product
+            lse[b, hq] = m + np.log(l)
+    return o, lse
+
+
 # ---------------------------------------------------------------------------
 # multi-segment split and the log-sum-exp merge
 # ---------------------------------------------------------------------------

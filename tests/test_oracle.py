@@ -799,3 +799,105 @@ def test_layernorm_mutants_are_caught(kind):
     assert not ok
     none = _ln_mutant("none")
     assert pin_ln_bruteforce(none) and pin_ln_closed_forms(none) and pin_ln_invariances(none) and pin_ln_numpy(none)
+
+
+# ---------------------------------------------------------------------------
+# grouped-query decode (query heads sharing key/value heads)
+# ---------------------------------------------------------------------------
+
+def _gqa_inputs(seed, B, Hq, Hkv, Lk, d):
+    r = np.random.default_rng(seed)
+    return r.normal(size=(B, Hq, d)), r.normal(size=(B, Hkv, Lk, d)), r.normal(size=(B, Hkv, Lk, d))
+
+
+def pin_gqa_bruteforce(fn):
+    """Pure Python (math.exp, math.fsum) on B = 2, Hq = 6, Hkv = 2 (G = 3), Lk = 5, d = 3."""
+    B, Hq, Hkv, Lk, d, sc = 2, 6, 2, 5, 3, 0.7
+    q, k, v = _gqa_inputs(41, B, Hq, Hkv, Lk, d)
+    o, lse = fn(q, k, v, sc)
+    G = Hq // Hkv
+    for b in range(B):
+        for hq in range(Hq):
+            j = hq // G
+            s = [sc * math.fsum(float(q[b, hq, t]) * float(k[b, j, i, t]) for t in range(d)) for i in range(Lk)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            l = math.fsum(e)
+            want = [math.fsum(e[i] * float(v[b, j, i, t]) for i in range(Lk)) / l for t in range(d)]
+            if max(abs(o[b, hq, t] - want[t]) for t in range(d)) > 1e-13:
+                return False
+            if abs(lse[b, hq] - (m + math.log(l))) > 1e-13:
+                return False
+    return True
+
+
+def pin_gqa_is_mha_with_repeated_kv(fn):
+    """Equal to the (separately pinned) multi-head attention oracle at Lq = 1 with
+    each key/value head repeated for its G consecutive query heads."""
+    for i, (B, Hq, Hkv, Lk, d) in enumerate(((1, 8, 2, 40, 16), (2, 4, 4, 17, 8), (1, 5, 1, 33, 4))):
+        q, k, v = _gqa_inputs(42 + i, B, Hq, Hkv, Lk, d)
+        o, lse = fn(q, k, v, 0.3)
+        G = Hq // Hkv
+        ro, rl = O.attention(q[:, :, None], np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), 0.3)
+        if np.max(np.abs(o - ro[:, :, 0])) > 1e-13 or np.max(np.abs(lse - rl[:, :, 0])) > 1e-13:
+            return False
+    return True
+
+
+def pin_gqa_closed_forms(fn):
+    q, k, v = _gqa_inputs(45, 2, 6, 3, 11, 4)
+    # q = 0: every key weighs the same, o = mean of the head's value rows, lse = ln Lk
+    o, lse = fn(np.zeros_like(q), k, v, 1.0)
+    want = np.repeat(v.mean(axis=2), 2, axis=1)
+    if np.max(np.abs(o - want)) > 1e-14 or np.max(np.abs(lse - math.log(11))) > 1e-14:
+        return False
+    # one key: o = v_0 exactly, lse = the single score
+    o, lse = fn(q, k[:, :, :1], v[:, :, :1], 0.5)
+    if not np.array_equal(o, np.repeat(v[:, :, 0], 2, axis=1)):
+        return False
+    s0 = 0.5 * np.einsum("bhd,bhd->bh", q, np.repeat(k[:, :, 0], 2, axis=1))
+    if np.max(np.abs(lse - s0)) > 1e-14:
+        return False
+    # no keys: (0, -inf)
+    o, lse = fn(q, k[:, :, :0], v[:, :, :0], 0.5)
+    return bool(np.all(o == 0) and np.all(lse == -np.inf))
+
+
+def test_gqa_pins():
+    assert pin_gqa_bruteforce(O.decode_gqa)
+    assert pin_gqa_is_mha_with_repeated_kv(O.decode_gqa)
+    assert pin_gqa_closed_forms(O.decode_gqa)
+
+
+def _gqa_mutant(kind):
+    def fn(q, k, v, scale):
+        q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+        B, Hq, d = q.shape
+        Hkv, Lk = k.shape[1], k.shape[2]
+        G = Hq // Hkv
+        o = np.zeros((B, Hq, v.shape[3]))
+        lse = np.full((B, Hq), -np.inf)
+        if Lk == 0:
+            return o, lse
+        for b in range(B):
+            for hq in range(Hq):
+                j = hq % Hkv if kind == "interleaved_heads" else hq // G
+                kh = k[b, j]
+                vh = kh if kind == "values_from_keys" else v[b, j]
+                s_ = (1.0 if kind == "no_scale" else scale) * (kh @ q[b, hq])
+                m = s_.max()
+                e = np.exp(s_ - m)
+                l = e.sum()
+                o[b, hq] = (e @ vh) / (1.0 if kind == "unnormalised" else l)
+                lse[b, hq] = (0.0 if kind == "lse_without_max" else m) + np.log(l)
+        return o, lse
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["interleaved_heads", "values_from_keys", "no_scale", "unnormalised",
+                                  "lse_without_max"])
+def test_gqa_mutants_are_caught(kind):
+    fn = _gqa_mutant(kind)
+    assert not (pin_gqa_bruteforce(fn) and pin_gqa_is_mha_with_repeated_kv(fn) and pin_gqa_closed_forms(fn))
+    none = _gqa_mutant("none")
+    assert pin_gqa_bruteforce(none) and pin_gqa_is_mha_with_repeated_kv(none) and pin_gqa_closed_forms(none)

@@ -204,7 +204,26 @@ EXTENSION_CONFIGS = {
     # softmax workload's shape; rows are drawn as the softmax rows are.
     "layernorm": dict(name="layernorm_f32_4096x32768", kind="layernorm", dtype="f32", rows=4096, cols=32768,
                       eps=1e-5, seed=7),
+    # Decode with grouped queries at the decode workload's cache length: 8 query
+    # heads per key/value head (grouped-query attention), and every query head
+    # on one shared cache (the MLA sharing pattern). q is drawn as [B, Hq, 1, d],
+    # k and v as [B, Hkv, Lk, d], per head like every other tensor.
+    "gqa_decode": dict(name="gqa_decode_bf16_B64_Hq64_Hkv8_Lk32768_d128_s4", kind="decode_gqa", dtype="bf16",
+                       B=64, Hq=64, Hkv=8, Lk=32768, d=128, scale=1.0 / math.sqrt(128), num_splits=4, seed=8),
+    "mla_decode": dict(name="shared_kv_decode_bf16_B64_Hq128_Hkv1_Lk32768_d128_s16", kind="decode_gqa",
+                       dtype="bf16", B=64, Hq=128, Hkv=1, Lk=32768, d=128, scale=1.0 / math.sqrt(128),
+                       num_splits=16, seed=9),
 }
+
+
+def gqa_inputs(cfg: dict, Lk: int | None = None):
+    """q [B, Hq, d], k and v [B, Hkv, Lk, d] of a grouped-query decode config
+    (raw bf16 bits as uint16), drawn per head."""
+    Lk = cfg["Lk"] if Lk is None else Lk
+    q = normal_tensor(cfg["seed"], TID_Q, cfg["B"], cfg["Hq"], 1, cfg["d"], cfg["dtype"])[:, :, 0]
+    k = normal_tensor(cfg["seed"], TID_K, cfg["B"], cfg["Hkv"], Lk, cfg["d"], cfg["dtype"])
+    v = normal_tensor(cfg["seed"], TID_V, cfg["B"], cfg["Hkv"], Lk, cfg["d"], cfg["dtype"])
+    return q, k, v
 
 
 def layernorm_affine(seed: int, cols: int):
