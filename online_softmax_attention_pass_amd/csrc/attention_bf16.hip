@@ -165,6 +165,17 @@ struct Smem {
   static constexpr int BYTES = 2 * BUF_ELEMS * 2;
 };
 
+// Barrier that publishes the workgroup's direct-to-LDS loads. Such a load
+// counts as complete (vmcnt) only in the wave that issued it, and the
+// compiler waits for it only before that same wave's own LDS reads; for the
+// other waves to read the data after the barrier, every wave must wait for
+// its own loads before it. Every barrier that hands a DMA-filled buffer to
+// other waves goes through here.
+__device__ __forceinline__ void publish_lds_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // Compiler-level pin: keeps the prefetch loads issued above it from being sunk
 // next to their use (which would turn the prefetch into a synchronous wait).
 __device__ __forceinline__ void pin_memory_order() { asm volatile("" ::: "memory"); }
@@ -1296,7 +1307,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         dma_one(khead, head_bytes, kb1, uint32_t(t1) * BN * D * 2, kv_off, wave * IPW, IPW);
         load_bits(bb1, t1, p1);
       }
-      __syncthreads();  // K(t0), K(t1), V(t0) resident
+      publish_lds_loads();  // K(t0), K(t1), V(t0) resident
       score_mfmas(kb0, s0);
       mask_tile(s0, t0, m0, p0, row_word(p0, bb0));
       {
@@ -1309,7 +1320,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       // leaves with the last tile's scores in s0 and its V in vb0 or vb1.
       bool last_in_vb1 = false;
       while (true) {
-        __syncthreads();  // loads of the previous step resident; kb0 and vb1 free
+        publish_lds_loads();  // loads of the previous step resident; kb0 and vb1 free
         if (t1 >= kt_end) break;
         int t2 = walk.next(t1 + 1, &m2, &p2);
         if (t2 < kt_end) {
@@ -1319,7 +1330,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         dma_one(vhead, head_bytes, vb1, uint32_t(t1) * BN * D * 2, vv_off, wave * IPW, IPW);
         step(kb1, vb0, s0, s1, t1, m1, p1, bb1);
 
-        __syncthreads();  // kb1 and vb0 free
+        publish_lds_loads();  // this step's loads resident; kb1 and vb0 free
         if (t2 >= kt_end) {
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) s0[mb] = s1[mb];

@@ -23,6 +23,15 @@ def _report(name, err_o, err_l, ref_o=None):
     print(f"\n[parity] {name}: max|dO| {err_o:.3e} max|dLSE| {err_l:.3e}{floor}", flush=True)
 
 
+def _same_again(first, again, what):
+    """The kernels have no atomics and no order-dependent reductions, so a second
+    call on the same inputs must give the same bits; a difference means a race
+    (for instance a shared-memory tile read before another wave's load landed)."""
+    import torch
+    for a, b in zip(first, again):
+        assert torch.equal(a, b), f"{what}: two calls on the same inputs differ"
+
+
 def _qkv_full(cfg):
     c = W.CONFIGS[cfg]
     return [W.normal_tensor(cfg, tid, c["B"], c["H"], L, c["d"], c["dtype"])
@@ -69,9 +78,12 @@ def test_config_attention_bf16(rf_gpu, cfg):
     q, k, v = _qkv_full(cfg)
     bm = W.config_block_mask(cfg)
     note(f"config {cfg} full")
-    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale=c["scale"], causal=c["causal"],
-                                     block_mask=None if bm is None else torch.from_numpy(bm).cuda())
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    bmd = None if bm is None else torch.from_numpy(bm).cuda()
+    o, lse = rf_gpu.rf_attention_fwd(qd, kd, vd, scale=c["scale"], causal=c["causal"], block_mask=bmd)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    _same_again((o, lse), rf_gpu.rf_attention_fwd(qd, kd, vd, scale=c["scale"], causal=c["causal"], block_mask=bmd),
+                f"config {cfg}")
     heads = [(0, 0), (c["B"] - 1, c["H"] - 1), (c["B"] // 2, c["H"] // 3), (0, c["H"] - 2)]
     rows = _sample_rows(c["Lq"], cfg)
     worst_o = worst_l = 0.0
@@ -102,8 +114,10 @@ def test_config4_decode(rf_gpu):
     vd = dev_bf16(v)
     del v
     note("config 4 full")
-    o, lse = rf_gpu.rf_attention_decode_splitkv(dev_bf16(q), kd, vd, scale=c["scale"], num_splits=S)
+    qd = dev_bf16(q)
+    o, lse = rf_gpu.rf_attention_decode_splitkv(qd, kd, vd, scale=c["scale"], num_splits=S)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    _same_again((o, lse), rf_gpu.rf_attention_decode_splitkv(qd, kd, vd, scale=c["scale"], num_splits=S), "config 4")
     heads = [(0, 0), (B - 1, H - 1), (17, 5), (40, 30), (63, 0), (5, 16)]
     worst_o = worst_l = 0.0
     refs = []
@@ -168,9 +182,10 @@ def test_extension_bitmap_full_size(rf_gpu):
                for t in (W.TID_Q, W.TID_K, W.TID_V))
     kinds, bits = W.extension_bitmap_mask()
     note("extension bitmap full size")
-    o, lse = rf_gpu.rf_attention_fwd_bitmap(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(kinds).cuda(),
-                                            torch.from_numpy(bits.view(np.int64)).cuda(), scale=c["scale"],
-                                            causal=c["causal"])
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(kinds).cuda(),
+            torch.from_numpy(bits.view(np.int64)).cuda())
+    o, lse = rf_gpu.rf_attention_fwd_bitmap(*args, scale=c["scale"], causal=c["causal"])
+    _same_again((o, lse), rf_gpu.rf_attention_fwd_bitmap(*args, scale=c["scale"], causal=c["causal"]), "bitmap")
     got_o, got_l = host_f64(o), host_f64(lse)
     rows = [0, 1, 63, 64, 511, 512, 513, 4095, 4096, 8000, 8191]
     e_o = e_l = 0.0
