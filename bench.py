@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the online-softmax attention path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads softmax,prefill,decode,sparse,attn_f32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads softmax,prefill,decode,...]
 
 One JSON line is printed. Its headline (``value``) is the row-softmax
 workload, fp32 4096 x 32768, in GB/s of algorithmic HBM traffic (one read and
@@ -10,6 +10,11 @@ one write per element); every workload that ran is also reported under
 (B4 H32 L4096 d128, TFLOP/s), split-KV bf16 decode (B64 H32 Lk32768 d128, 16
 splits, GB/s), block-sparse bf16 attention (B2 H16 L8192 d64, TFLOP/s on
 active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds).
+Extension workloads: element bitmaps in partial tiles (B2 H16 L8192 d64,
+TFLOP/s), row layer normalisation (fp32 4096 x 32768, GB/s), and decode with
+grouped queries at Lk 32768, d 128: 8 query heads per key/value head (B64 Hq64
+Hkv8, 4 splits) and 128 query heads on one cache (B64 Hq128 Hkv1, 16 splits),
+in GB/s with TFLOP/s alongside.
 
 Timing: inputs are resident in HBM before the timed region; W untimed
 warm-up calls; then K calls, each bracketed by HIP events recorded on the
@@ -41,7 +46,7 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 KERNEL_SOURCES = {
     "copy": None, "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip", "bitmap": "attention_bf16.hip",
-    "layernorm": "layernorm_rows.hip",
+    "layernorm": "layernorm_rows.hip", "gqa": "attention_bf16.hip", "mla": "attention_bf16.hip",
 }
 
 
@@ -225,6 +230,38 @@ def setup_decode(rf, torch, W):
                 extra={"workspace_bytes_round_trip": int(2 * n * S * (d + 1) * 4)})
 
 
+def _setup_gqa(rf, torch, W, name):
+    c = W.EXTENSION_CONFIGS[name]
+    B, Hq, Hkv, Lk, d, S = c["B"], c["Hq"], c["Hkv"], c["Lk"], c["d"], c["num_splits"]
+    log(f"{name}: generating {2 * B * Hkv * Lk * d * 2 / 2**30:.1f} GiB of K/V on the host")
+    up = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    qh, kh, vh = W.gqa_inputs(c)
+    q, k, v = up(qh), up(kh), up(vh)
+    del qh, kh, vh
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws_bytes = rf.rf_attention_decode_gqa_workspace_size(B, Hq, d, S)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    nbytes = 2 * B * Hkv * Lk * d * 2 + 2 * B * Hq * d * 2 + B * Hq * 4
+    n = B * Hq
+    o_parts = ws[: n * S * d * 4].view(torch.float32).view(n, S, d)
+    lse_off = -(-n * S * d * 4 // 256) * 256
+    lse_parts = ws[lse_off: lse_off + n * S * 4].view(torch.float32).view(n, S)
+    merge = lambda: rf.rf_lse_merge(o_parts, lse_parts, out_dtype=torch.bfloat16, out=o.view(n, d), lse=lse.view(n))
+    return dict(fn=lambda: rf.rf_attention_decode_gqa(q, k, v, scale=c["scale"], num_splits=S, workspace=ws,
+                                                      out=o, lse=lse),
+                work=nbytes, unit="GB/s", bound="hbm", keep=(q, k, v, o, lse, ws), cfg=c, subtract=merge,
+                flops=4 * B * Hq * Lk * d, extra={"workspace_bytes_round_trip": int(2 * n * S * (d + 1) * 4)})
+
+
+def setup_gqa_decode(rf, torch, W):
+    return _setup_gqa(rf, torch, W, "gqa_decode")
+
+
+def setup_mla_decode(rf, torch, W):
+    return _setup_gqa(rf, torch, W, "mla_decode")
+
+
 def setup_attn_f32(rf, torch, W):
     c = W.CONFIGS[1]
     q, k, v = (torch.from_numpy(W.normal_tensor(1, t, 1, 1, 128, 64, "f32")).cuda()
@@ -246,7 +283,7 @@ def setup_copy(rf, torch, W):
                 cfg={"name": "calibration_copy_f32_1GiB", "dtype": "f32"})
 
 
-SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse,
+SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse, "gqa": setup_gqa_decode, "mla": setup_mla_decode,
           "attn_f32": setup_attn_f32}
 
 
@@ -284,7 +321,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm")
+    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -331,6 +368,8 @@ def main():
         if merge_ms is not None:
             r["merge_ms"] = round(merge_ms, 5)
             r["partial_kernel_ms"] = round(kern_ms, 5)
+        if "flops" in s:
+            r["tflops"] = round(s["flops"] / (call_ms * 1e-3) / 1e12, 3)
         r.update(s.get("extra", {}))
         results[name] = r
         cfgs[name] = s["cfg"]

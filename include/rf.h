@@ -188,6 +188,45 @@ int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * Bytes of device workspace that rf_attention_decode_gqa needs: 0 when
+ * num_splits == 1 (no partials), else B*Hq*num_splits*(d + 1) fp32 values laid
+ * out and rounded as for rf_attention_decode_splitkv. Returns 0 for invalid
+ * arguments too.
+ */
+size_t rf_attention_decode_gqa_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * Decode with grouped queries: Hq = G * Hkv query heads, one token each, where
+ * query head hq attends the cached keys and values of head hq / G (the G
+ * consecutive query heads G j .. G j + G - 1 share key/value head j). Hkv = 1
+ * is the sharing pattern of MLA decode: every query head reads one cache. The
+ * result per query head is exactly rf_attention_decode_splitkv's with H = Hq
+ * and each key/value head repeated G times; here each key/value tile is read
+ * once for its G query heads, which are the rows of one matrix-core tile.
+ * Source: RedFuser page, 4. Résultats Expérimentaux (MHA and MLA workloads)
+ * and 3. Contributions clés (multi-segment strategy, merge of partials).
+ *   q, o       : [B, Hq, d] of `dtype` (o written);  k, v : [B, Hkv, Lk, d].
+ *   lse        : [B, Hq] fp32, written; may be NULL.
+ *   num_splits : 1 .. 1024. Keys go in tiles of 64; split s covers tiles
+ *                [s T, (s + 1) T), T = ceil(ceil(Lk / 64) / num_splits);
+ *                trailing splits may be empty. Each split yields a normalised
+ *                fp32 partial and its LSE, merged as rf_lse_merge does. With
+ *                num_splits == 1 the result is written directly and no
+ *                workspace is used (workspace may be NULL).
+ *   workspace  : for num_splits > 1, a device buffer of at least
+ *                rf_attention_decode_gqa_workspace_size(B, Hq, d, num_splits)
+ *                bytes, 256-byte aligned, untouched until the work completes.
+ * No mask applies. Lk == 0 gives O = 0, LSE = -inf. The latent widths of MLA
+ * (576-wide keys, 512-wide values) are not supported.
+ * Supported: RF_BF16 with d in {64, 128} and Lk * d * 2 < 2^31.
+ * Errors: RF_ERR_INVALID_ARG (including Hq not a multiple of Hkv),
+ * RF_ERR_UNSUPPORTED, RF_ERR_WORKSPACE, RF_ERR_HIP.
+ */
+int rf_attention_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                            int Hkv, int Lk, int d, float scale, int num_splits, void* workspace,
+                            size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * Log-sum-exp merge of normalised partial results (the merge step of the
  * multi-segment strategy; order-free because the (O, lse) pairs form a
  * commutative monoid with identity (anything, -inf)).
@@ -214,7 +253,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 2
+#define RF_ABI_VERSION 3
 int rf_abi_version(void);
 
 #ifdef __cplusplus

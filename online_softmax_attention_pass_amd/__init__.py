@@ -17,7 +17,8 @@ import os
 __all__ = [
     "RF_F32", "RF_BF16", "RFError", "load", "library_path",
     "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_decode_splitkv",
-    "rf_attention_decode_splitkv_workspace_size", "rf_lse_merge", "rf_abi_version",
+    "rf_attention_decode_splitkv_workspace_size", "rf_attention_decode_gqa", "rf_attention_decode_gqa_workspace_size",
+    "rf_lse_merge", "rf_abi_version",
 ]
 
 RF_F32, RF_BF16 = 0, 1
@@ -56,6 +57,8 @@ def load():
         "rf_attention_fwd_bitmap": ([P, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P], I),
         "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_splitkv": ([P, P, P, P, P, I, I, I, I, F, I, P, SZ, I, P], I),
+        "rf_attention_decode_gqa_workspace_size": ([I, I, I, I], SZ),
+        "rf_attention_decode_gqa": ([P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
         "rf_status_string": ([I], ctypes.c_char_p),
         "rf_last_error_message": ([], ctypes.c_char_p),
@@ -268,6 +271,38 @@ def rf_attention_decode_splitkv(q, k, v, scale=None, num_splits=16, workspace=No
                                          float(scale), num_splits, _ptr(workspace), nbytes, _dtype_code(q),
                                          _stream(dev))
     _check(st, "rf_attention_decode_splitkv")
+    return o, lse
+
+
+def rf_attention_decode_gqa_workspace_size(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(load().rf_attention_decode_gqa_workspace_size(B, Hq, d, num_splits))
+
+
+def rf_attention_decode_gqa(q, k, v, scale=None, num_splits=1, workspace=None, out=None, lse=None, want_lse=True):
+    """Grouped-query decode. q [B,Hq,d]; k, v [B,Hkv,Lk,d] (bf16), Hq a multiple of Hkv.
+    Returns (o [B,Hq,d], lse [B,Hq])."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k, v [B, Hkv, Lk, d]")
+    B, Hq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, Lk, d) or v.shape != (B, Hkv, Lk, d):
+        raise ValueError("k, v must be [B, Hkv, Lk, d] matching q")
+    ws_bytes = rf_attention_decode_gqa_workspace_size(B, Hq, d, num_splits)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    dev = _dev(q, k, v, o, lse, workspace)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.rf_attention_decode_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Lk, d,
+                                     float(scale), num_splits, _ptr(workspace), nbytes, _dtype_code(q),
+                                     _stream(dev))
+    _check(st, "rf_attention_decode_gqa")
     return o, lse
 
 

@@ -839,12 +839,20 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 // a tile's row maximum exceeds it by more than 2^kRescaleSlack. The rescale
 // of O waits for the P.V product that precedes it in phase B.
 // ---------------------------------------------------------------------------
-template <int D, int NW, int WPE, bool BITS>
+//
+// SPLIT: split-KV partials. Item = (head, split, query tile); split s visits
+// key tiles [s kt_split, (s + 1) kt_split) only, and writes its output,
+// normalised, in fp32 with its LSE into ws_o [head rows, n_splits, D] and
+// ws_lse [head rows, n_splits] for a log-sum-exp merge. Used for decode with
+// grouped queries, where the query heads sharing one key/value head are the
+// rows of the query tile.
+template <int D, int NW, int WPE, bool BITS, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
     const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group,
-    int64_t item_base, const uint64_t* __restrict__ tile_bits, uint32_t bits_bytes) {
+    int64_t item_base, const uint64_t* __restrict__ tile_bits, uint32_t bits_bytes, int n_splits = 1,
+    int kt_split = 0, float* __restrict__ ws_o = nullptr, float* __restrict__ ws_lse = nullptr) {
   constexpr int BN = 64;
   constexpr int BM = 32 * NW;
   constexpr int KCH = D / 8;
@@ -894,7 +902,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // this launch, permuted by work_item within the launch.
   {
     const int64_t item = item_base + work_item(blockIdx.x, n_items, per_xcd, xcd_remap, n_qt, head_group);
-    const int64_t bh = item / n_qt;
+    const int64_t bhs = item / n_qt;
+    const int64_t bh = SPLIT ? bhs / n_splits : bhs;
+    const int split = SPLIT ? int(bhs % n_splits) : 0;
     const int qr = int(item % n_qt);
     const int q0 = (causal ? (n_qt - 1 - qr) : qr) * BM;
     const int q0w = q0 + 32 * wave;
@@ -904,7 +914,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
     int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
     if (last_key > Lk - 1) last_key = Lk - 1;
-    const int kt_end = last_key < 0 ? 0 : int(last_key / BN) + 1;
+    const int kt_all = last_key < 0 ? 0 : int(last_key / BN) + 1;
+    const int kt_begin = SPLIT ? split * kt_split : 0;
+    const int kt_end = SPLIT ? min(kt_all, kt_begin + kt_split) : kt_all;
     TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
                     min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
     walk.bits = BITS;
@@ -1297,7 +1309,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         dma_bits(tile_bits, bits_bytes, bb, off);
       }
     };
-    int t0 = walk.next(0, &m0, &p0);
+    int t0 = walk.next(kt_begin, &m0, &p0);
     if (t0 < kt_end) {
       int t1 = walk.next(t0 + 1, &m1, &p1);
       dma_one(khead, head_bytes, kb0, uint32_t(t0) * BN * D * 2, kv_off, wave * IPW, IPW);
@@ -1358,6 +1370,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int qi = q0w + l32;
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_rtot : 0.f;
+    if constexpr (SPLIT) {
+      // fp32 partial: lane (row l32, half h) holds d = 32 db + 16 pp + 8 sel + 4 h + i
+      // in acc_o[db][8 pp + 4 sel + i]; 16-byte stores of 4 consecutive d.
+      if (qi < Lq) {
+        const int64_t prow = (bh * Lq + qi) * n_splits + split;
+        float* orow = ws_o + prow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) {
+            const float4 x = make_float4(acc_o[db][r] * inv, acc_o[db][r + 1] * inv, acc_o[db][r + 2] * inv,
+                                         acc_o[db][r + 3] * inv);
+            *reinterpret_cast<float4*>(orow + 32 * db + 2 * r + 4 * h) = x;
+          }
+        if (h == 0) ws_lse[prow] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+      }
+      return;
+    }
     // Output: each wave's 32 rows are one contiguous block of O. Lanes l and
     // l + 32 hold alternate 8-byte pieces of a row; one v_permlane32_swap per
     // dword gives each lane a 16-byte run, which goes through this wave's own
@@ -1741,6 +1771,21 @@ hipError_t launch_pp(const void* q, const void* k, const void* v, void* o, float
   return hipGetLastError();
 }
 
+// Score coefficient in log2 units. The kernels take it positive: a negative
+// scale negates Q as it is loaded (q_mode 1), a zero scale zeroes it (q_mode 2).
+inline float score_coef(float scale, int* q_mode) {
+  float c = float(double(scale) * 1.4426950408889634);
+  *q_mode = 0;
+  if (scale < 0.f) {
+    *q_mode = 1;
+    c = -c;
+  } else if (scale == 0.f) {
+    *q_mode = 2;
+    c = 1.f;
+  }
+  return c;
+}
+
 template <int D, int NW, int WPE, int BN, bool SP, bool BITS = false>
 hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
                       int Lk, float scale, int causal, const uint8_t* block_mask, hipStream_t stream,
@@ -1749,14 +1794,7 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
   const int n_qt = (Lq + BM - 1) / BM;
   const int64_t n_items = int64_t(B) * H * n_qt;
   int q_mode = 0;
-  float c = float(double(scale) * 1.4426950408889634);
-  if (scale < 0.f) {
-    q_mode = 1;
-    c = -c;
-  } else if (scale == 0.f) {
-    q_mode = 2;
-    c = 1.f;
-  }
+  const float c = score_coef(scale, &q_mode);
   const int64_t cap = 1LL << 22;
   const unsigned grid = unsigned(n_items < cap ? n_items : cap);
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
@@ -1784,7 +1822,44 @@ hipError_t launch_dma(const void* q, const void* k, const void* v, void* o, floa
   return hipGetLastError();
 }
 
+
+// Split-KV partials (no mask): items (head, split, query tile), key tiles
+// divided into n_splits contiguous ranges of ceil(n_tiles / n_splits) tiles.
+template <int D, int NW, int WPE>
+hipError_t launch_split(const void* q, const void* k, const void* v, float* ws_o, float* ws_lse, int n_heads, int Lq,
+                        int Lk, float scale, int n_splits, hipStream_t stream) {
+  constexpr int BM = 32 * NW;
+  const int n_qt = (Lq + BM - 1) / BM;
+  const int n_kt = (Lk + 63) / 64;
+  const int kt_split = (n_kt + n_splits - 1) / n_splits;
+  const int64_t n_items = int64_t(n_heads) * n_splits * n_qt;
+  int q_mode = 0;
+  const float c = score_coef(scale, &q_mode);
+  const int64_t cap = 1LL << 22;
+  const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
+  for (int64_t base = 0; base < n_items; base += cap) {
+    const int64_t n = n_items - base < cap ? n_items - base : cap;
+    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, false, true>), dim3(unsigned(n)), dim3(NW * 64), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), nullptr, nullptr, Lq, Lk, c, q_mode, 0, nullptr, n_qt, n,
+                       xcd_remap, 1, base, nullptr, 0u, n_splits, kt_split, ws_o, ws_lse);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_attention_bf16_split(const void* q, const void* k, const void* v, float* ws_o, float* ws_lse,
+                                       int n_heads, int Lq, int Lk, int d, float scale, int n_splits,
+                                       hipStream_t stream) {
+  if (d == 128)
+    return launch_split<128, RF_ATT_NW_D128, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale,
+                                                               n_splits, stream);
+  return launch_split<64, RF_ATT_NW_D64, RF_ATT_WPE_D64>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits,
+                                                          stream);
+}
 
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,

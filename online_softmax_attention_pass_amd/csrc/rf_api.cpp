@@ -265,6 +265,68 @@ int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, voi
   }
 }
 
+size_t rf_attention_decode_gqa_workspace_size(int B, int Hq, int d, int num_splits) {
+  DecodeWs w;
+  if (!decode_ws_layout(B, Hq, d, num_splits, w)) return 0;
+  return num_splits == 1 ? 0 : w.total;
+}
+
+int rf_attention_decode_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                            int Hkv, int Lk, int d, float scale, int num_splits, void* workspace,
+                            size_t workspace_bytes, int dtype, void* stream) {
+  const char* name = "rf_attention_decode_gqa";
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+    if (B < 0 || Hq < 0 || Lk < 0)
+      return fail(RF_ERR_INVALID_ARG, "%s: negative size (B=%d Hq=%d Lk=%d)", name, B, Hq, Lk);
+    if (Hkv < 1 || Hq % Hkv != 0)
+      return fail(RF_ERR_INVALID_ARG, "%s: Hq = %d is not a multiple of Hkv = %d >= 1", name, Hq, Hkv);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "%s: d = %d < 1", name, d);
+    if (num_splits < 1 || num_splits > 1024)
+      return fail(RF_ERR_INVALID_ARG, "%s: num_splits = %d outside 1..1024", name, num_splits);
+    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "%s: scale is not finite", name);
+    if (dtype != RF_BF16) return fail(RF_ERR_UNSUPPORTED, "%s: only bf16 is supported", name);
+    if (d != 64 && d != 128) return fail(RF_ERR_UNSUPPORTED, "%s: d must be 64 or 128, got %d", name, d);
+    int64_t nq = 1, nk = 1;
+    if (!mul_ok(nq, B) || !mul_ok(nq, Hq) || !mul_ok(nq, d) || !mul_ok(nq, 2) || !mul_ok(nk, B) ||
+        !mul_ok(nk, Hkv) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, 2))
+      return fail(RF_ERR_INVALID_ARG, "%s: tensor size overflows int64", name);
+    if (int64_t(Lk) * d * 2 > INT32_MAX)
+      return fail(RF_ERR_UNSUPPORTED, "%s: needs Lk * d * 2 < 2^31 bytes per key/value head", name);
+    if (int64_t(B) * Hq > INT32_MAX) return fail(RF_ERR_UNSUPPORTED, "%s: B * Hq must be below 2^31", name);
+    DecodeWs w;
+    if (!decode_ws_layout(B, Hq, d, num_splits, w)) return fail(RF_ERR_INVALID_ARG, "%s: workspace size overflows", name);
+    if (int64_t(B) * Hq == 0) return ok();
+    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL q or o", name);
+    if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "%s: NULL k or v", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
+      return fail(RF_ERR_UNSUPPORTED, "%s: needs 16-byte aligned q, k, v and 8-byte aligned o", name);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "%s: lse misaligned", name);
+    if (num_splits > 1 && (workspace == nullptr || workspace_bytes < w.total || !aligned(workspace, 256)))
+      return fail(RF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", name,
+                  w.total, workspace_bytes, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int G = Hq / Hkv;
+    // q [B, Hq, d] is [B, Hkv, G, d]: the G query heads of a key/value head are
+    // the rows of its query tile.
+    if (num_splits == 1)
+      return hip_status(rf::launch_attention_bf16(q, k, v, o, lse, B, Hkv, G, Lk, d, scale, false, nullptr,
+                                                  nullptr, s),
+                        name);
+    float* o_parts = static_cast<float*>(workspace);
+    float* lse_parts = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lse_off);
+    hipError_t e =
+        rf::launch_attention_bf16_split(q, k, v, o_parts, lse_parts, B * Hkv, G, Lk, d, scale, num_splits, s);
+    if (e != hipSuccess) return hip_status(e, "rf_attention_decode_gqa (partials)");
+    e = rf::launch_lse_merge(o_parts, lse_parts, o, lse, int64_t(B) * Hq, num_splits, d, RF_BF16, s);
+    return hip_status(e, "rf_attention_decode_gqa (merge)");
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
+  }
+}
+
 int rf_lse_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int64_t n_rows, int num_splits,
                  int d, int out_dtype, void* stream) {
   try {

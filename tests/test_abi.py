@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 2
+    assert lib.rf_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -191,6 +191,42 @@ def dec(lib, **kw):
 ])
 def test_decode_validation(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+def test_gqa_workspace_size(lib):
+    B, Hq, d, S = 64, 64, 128, 4
+    assert lib.rf_attention_decode_gqa_workspace_size(B, Hq, d, S) == \
+        lib.rf_attention_decode_splitkv_workspace_size(B, Hq, d, S)
+    assert lib.rf_attention_decode_gqa_workspace_size(B, Hq, d, 1) == 0      # written directly
+    assert lib.rf_attention_decode_gqa_workspace_size(-1, Hq, d, 4) == 0
+    assert lib.rf_attention_decode_gqa_workspace_size(1, 1, 64, 1025) == 0
+
+
+GQA = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=4, Hq=16, Hkv=2, Lk=1000, d=128, scale=0.1, S=8, ws=FAKE,
+           ws_bytes=1 << 30, dtype=BF16)
+
+
+def gqa(lib, **kw):
+    a = dict(GQA, **kw)
+    return lib.rf_attention_decode_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Lk"],
+                                       a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), INVALID), (dict(B=-1), INVALID), (dict(Hq=-2), INVALID), (dict(Lk=-1), INVALID),
+    (dict(Hkv=0), INVALID), (dict(Hkv=3), INVALID), (dict(Hkv=32), INVALID), (dict(d=0), INVALID),
+    (dict(S=0), INVALID), (dict(S=1025), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(Lk=1 << 23), UNSUP), (dict(B=1 << 27), UNSUP),
+    (dict(q=NUL), INVALID), (dict(o=NUL), INVALID), (dict(k=NUL), INVALID), (dict(v=NUL), INVALID),
+    (dict(lse=P(0x10002)), INVALID),
+    (dict(ws=NUL), WS), (dict(ws_bytes=100), WS), (dict(ws=P(0x10010)), WS),
+    (dict(k=P(0x10008)), UNSUP), (dict(o=P(0x10004)), UNSUP),
+    (dict(B=0), OK), (dict(Hq=0, ws=NUL, ws_bytes=0), OK),
+])
+def test_gqa_validation(lib, kw, code):
+    assert gqa(lib, **kw) == code
+    if code != OK:
+        assert "rf_attention_decode_gqa" in _msg(lib)
 
 
 @pytest.mark.parametrize("args,code", [

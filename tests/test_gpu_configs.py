@@ -216,3 +216,39 @@ def test_extension_layernorm_full_size(rf_gpu):
     assert np.all(np.abs(host_f64(mean) - rm_all) <= 1e-6 * np.abs(rm_all) + 1e-6)
     assert np.all(np.abs(host_f64(rstd) - rr_all) <= 1e-6 * np.abs(rr_all) + 1e-6)
     _report("extension layernorm", e, 0.0)
+
+
+@pytest.mark.parametrize("name", ["gqa_decode", "mla_decode"])
+def test_extension_gqa_full_size(rf_gpu, name):
+    """Grouped-query decode at full size (Lk 32768, d 128): 8 query heads per
+    key/value head, and 128 query heads on one cache; sampled query heads
+    against the oracle."""
+    import torch
+    c = W.EXTENSION_CONFIGS[name]
+    B, Hq, Hkv, Lk, d, S = c["B"], c["Hq"], c["Hkv"], c["Lk"], c["d"], c["num_splits"]
+    G = Hq // Hkv
+    note(f"extension {name}: generating inputs")
+    q, k, v = W.gqa_inputs(c)
+    kd, vd = dev_bf16(k), dev_bf16(v)
+    note(f"extension {name} full")
+    qd = dev_bf16(q)
+    o, lse = rf_gpu.rf_attention_decode_gqa(qd, kd, vd, scale=c["scale"], num_splits=S)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    _same_again((o, lse), rf_gpu.rf_attention_decode_gqa(qd, kd, vd, scale=c["scale"], num_splits=S), name)
+    picks = [(0, 0), (B - 1, Hq - 1), (17, G - 1), (40, G % Hq), (63, Hq // 2), (5, 3)]
+    worst_o = worst_l = 0.0
+    refs = []
+    for b, hq in picks:
+        j = hq // G
+        ref_o, ref_lse = O.decode_gqa(O.bf16_bits_to_f64(q[b:b + 1, hq:hq + 1]), O.bf16_bits_to_f64(k[b:b + 1, j:j + 1]),
+                                      O.bf16_bits_to_f64(v[b:b + 1, j:j + 1]), c["scale"])
+        got = host_f64(o[b, hq])
+        worst_o = max(worst_o, max_abs_err(got, ref_o[0, 0]))
+        worst_l = max(worst_l, max_abs_err(host_f64(lse[b, hq:hq + 1]), ref_lse[0]))
+        # Beyond the absolute gate: over 32768 keys the rounding of P to bf16
+        # averages out, so each element is within one bf16 rounding of the exact
+        # value plus 1e-4 (at |O| ~ 0.03 the absolute gate alone is loose).
+        assert np.all(np.abs(got - ref_o[0, 0]) <= 2.0 ** -8 * np.abs(ref_o[0, 0]) + 1e-4), (name, b, hq)
+        refs.append(ref_o[0, 0])
+    _report(f"extension {name} ({len(picks)} query heads)", worst_o, worst_l, np.concatenate(refs))
+    assert worst_o <= 1e-2 and worst_l <= 1e-3
