@@ -8,6 +8,7 @@ sides use is ``workloads`` (seeded input draws, no arithmetic of the method).
 """
 from .oracle import (  # noqa: F401
     attention,
+    attention_score_mod,
     bf16_bits_to_f64,
     decode_gqa,
     decode_splitkv_partials,

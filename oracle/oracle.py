@@ -219,6 +219,54 @@ def attention(q, k, v, scale: float, causal: bool = False, block_mask=None,
     return O, LSE
 
 
+def attention_score_mod(q, k, v, scale: float, causal: bool = False, block_mask=None, window: int = 0,
+                        alibi_slopes=None, softcap: float = 0.0, q_rows=None):
+    """Attention with score modifications, in fp64: the FlexAttention variants
+    the FLASHLIGHT page benchmarks (Risultati: ALiBi, Softcap, Causal, Sliding
+    Window; the Softcap attention of LLaMa-3.2-1B under vLLM).
+
+    q: [B, H, Lq, d]; k, v: [B, H, Lk, d]. For head h, query row i at position
+    p_i = i + Lk - Lq (bottom-right, as the causal rule) and key j:
+      s = scale * (q_i . k_j)
+      softcap > 0     : s <- softcap * tanh(s / softcap)
+      alibi_slopes [H]: s <- s + slope_h * (j - p_i)
+      visible(i, j)   = element_mask(...)  and  (window == 0  or  j > p_i - window)
+    then the masked softmax in three passes and O = P V, LSE = m + ln l; a row
+    with no visible key gives O = 0, LSE = -inf. Returns (O, LSE) for the rows
+    q_rows (all rows by default).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    rows = np.arange(Lq) if q_rows is None else np.asarray(q_rows)
+    pos = rows[:, None] + (Lk - Lq)                        # query positions
+    j = np.arange(Lk)[None, :]
+    vis = element_mask(Lq, Lk, causal, block_mask, q_rows=rows)
+    if window:
+        vis &= j > pos - window
+    O = np.zeros((B, H, len(rows), v.shape[3]))
+    LSE = np.full((B, H, len(rows)), NEG_INF)
+    for b in range(B):
+        for h in range(H):
+            S = scale * (q[b, h, rows] @ k[b, h].T)         # explicit GEMM
+            if softcap > 0:
+                S = softcap * np.tanh(S / softcap)
+            if alibi_slopes is not None:
+                S = S + float(alibi_slopes[h]) * (j - pos)
+            S = np.where(vis, S, NEG_INF)
+            m = S.max(axis=1) if Lk else np.full(len(rows), NEG_INF)    # pass 1
+            live = np.isfinite(m)
+            m0 = np.where(live, m, 0.0)
+            E = np.exp(S - m0[:, None])
+            l = E.sum(axis=1)                                  # pass 2
+            l1 = np.where(live, l, 1.0)
+            O[b, h] = np.where(live[:, None], (E / l1[:, None]) @ v[b, h], 0.0)   # pass 3, P V
+            LSE[b, h] = np.where(live, m0 + np.log(l1), NEG_INF)
+    return O, LSE
+
+
 def decode_gqa(q, k, v, scale: float):
     """Decode with grouped queries, in fp64: one token per query head, and
     query heads that share key/value heads (RedFuser page, 4. Résultats

@@ -901,3 +901,154 @@ def test_gqa_mutants_are_caught(kind):
     assert not (pin_gqa_bruteforce(fn) and pin_gqa_is_mha_with_repeated_kv(fn) and pin_gqa_closed_forms(fn))
     none = _gqa_mutant("none")
     assert pin_gqa_bruteforce(none) and pin_gqa_is_mha_with_repeated_kv(none) and pin_gqa_closed_forms(none)
+
+
+# ---------------------------------------------------------------------------
+# score modifications: softcap, ALiBi bias, element-level sliding window
+# ---------------------------------------------------------------------------
+
+def _mod_inputs(seed, B, H, Lq, Lk, d, qscale=1.0):
+    r = np.random.default_rng(seed)
+    return qscale * r.normal(size=(B, H, Lq, d)), r.normal(size=(B, H, Lk, d)), r.normal(size=(B, H, Lk, d))
+
+
+def pin_mod_bruteforce(fn):
+    """Pure Python (math.tanh, math.exp, math.fsum): causal with Lq < Lk, window 3,
+    two ALiBi slopes and a softcap that bends the scores (|s| up to ~6 vs cap 2)."""
+    B, H, Lq, Lk, d, sc, cap, W = 1, 2, 3, 6, 4, 0.9, 2.0, 3
+    slopes = [0.5, 0.25]
+    q, k, v = _mod_inputs(51, B, H, Lq, Lk, d, qscale=2.0)
+    o, lse = fn(q, k, v, sc, causal=True, window=W, alibi_slopes=np.array(slopes), softcap=cap)
+    for h in range(H):
+        for i in range(Lq):
+            p = i + Lk - Lq
+            keys = [j for j in range(Lk) if j <= p and j > p - W]
+            s = []
+            for j in keys:
+                x = sc * math.fsum(float(q[0, h, i, t]) * float(k[0, h, j, t]) for t in range(d))
+                s.append(cap * math.tanh(x / cap) + slopes[h] * (j - p))
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            l = math.fsum(e)
+            for t in range(d):
+                want = math.fsum(e[n] * float(v[0, h, keys[n], t]) for n in range(len(keys))) / l
+                if abs(o[0, h, i, t] - want) > 1e-13:
+                    return False
+            if abs(lse[0, h, i] - (m + math.log(l))) > 1e-13:
+                return False
+    return True
+
+
+def pin_mod_reductions(fn):
+    """No modification equals the (separately pinned) attention oracle; a huge
+    softcap, zero slopes and a window covering every key change nothing; a
+    window equals the same mask given as element bitmaps (the oracle's
+    bitmap decoding, a separate code path)."""
+    q, k, v = _mod_inputs(52, 1, 2, 70, 150, 8)
+    ref = O.attention(q, k, v, 0.4, True)
+    for kw in (dict(), dict(softcap=1e7), dict(alibi_slopes=np.zeros(2)), dict(window=150)):
+        got = fn(q, k, v, 0.4, causal=True, **kw)
+        if np.max(np.abs(got[0] - ref[0])) > 1e-9 or np.max(np.abs(got[1] - ref[1])) > 1e-9:
+            return False
+    W = 37
+    Lq, Lk = 70, 150
+    i = np.arange(Lq)[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    vis = (j <= i) & (j > i - W)
+    nI, nJ = -(-Lq // 64), -(-Lk // 64)
+    pad = np.zeros((nI * 64, nJ * 64), bool)
+    pad[:Lq, :Lk] = vis
+    tiles = pad.reshape(nI, 64, nJ, 64).transpose(0, 2, 1, 3)
+    bits = (tiles.astype(np.uint64) << np.arange(64, dtype=np.uint64)).sum(axis=-1, dtype=np.uint64)
+    kinds = np.full((nI, nJ), 2, np.uint8)
+    ref = O.attention(q, k, v, 0.4, False, kinds, tile_bits=bits)
+    got = fn(q, k, v, 0.4, causal=True, window=W)
+    return bool(np.max(np.abs(got[0] - ref[0])) < 1e-12 and np.max(np.abs(got[1] - ref[1])) < 1e-12)
+
+
+def pin_mod_closed_forms(fn):
+    Lq = Lk = 40
+    d = Lk
+    # ALiBi with q = 0, causal: P_ij = e^{-a (p - j)} / sum_{t=0}^{p} e^{-a t}; with V = I, O is P itself
+    a = 0.3
+    q = np.zeros((1, 1, Lq, d))
+    k = np.random.default_rng(53).normal(size=(1, 1, Lk, d))
+    v = np.eye(Lk)[None, None]
+    o, lse = fn(q, k, v, 1.0, causal=True, alibi_slopes=np.array([a]))
+    for i in (0, 1, 17, Lq - 1):
+        z = (1 - math.exp(-a * (i + 1))) / (1 - math.exp(-a))
+        want = np.zeros(d)
+        want[:i + 1] = np.exp(-a * (i - np.arange(i + 1))) / z
+        if np.max(np.abs(o[0, 0, i] - want)) > 1e-14 or abs(lse[0, 0, i] - math.log(z)) > 1e-14:
+            return False
+    # window 1, causal: only the diagonal key, O = v_p exactly, LSE = its score
+    q, k, v = _mod_inputs(54, 1, 2, 5, 9, 4)
+    o, lse = fn(q, k, v, 0.7, causal=True, window=1)
+    p = np.arange(5) + 4
+    if not np.array_equal(o[0], v[0][:, p]):
+        return False
+    s = 0.7 * np.einsum("hid,hid->hi", q[0], k[0][:, p])
+    if np.max(np.abs(lse[0] - s)) > 1e-14:
+        return False
+    # a softcap bounds every logit: |s'| < cap, so P stays within e^{2 cap} of uniform
+    q, k, v = _mod_inputs(55, 1, 1, 4, 30, 8, qscale=5.0)
+    cap = 0.1
+    o, lse = fn(q, k, v, 1.0, softcap=cap)
+    dev = np.abs(o[0, 0] - v[0, 0].mean(axis=0))
+    return bool(np.all(dev <= (math.exp(2 * cap) - 1) * np.abs(v).max()) and
+                np.all(np.abs(lse - math.log(30)) <= cap))
+
+
+def test_score_mod_pins():
+    assert pin_mod_bruteforce(O.attention_score_mod)
+    assert pin_mod_reductions(O.attention_score_mod)
+    assert pin_mod_closed_forms(O.attention_score_mod)
+
+
+def _mod_mutant(kind):
+    def fn(q, k, v, scale, causal=False, block_mask=None, window=0, alibi_slopes=None, softcap=0.0, q_rows=None):
+        q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+        B, H, Lq, d = q.shape
+        Lk = k.shape[2]
+        pos = np.arange(Lq)[:, None] + (Lk - Lq)
+        j = np.arange(Lk)[None, :]
+        vis = O.element_mask(Lq, Lk, causal, block_mask)
+        if window:
+            vis &= (j >= pos - window) if kind == "window_off_by_one" else (j > pos - window)
+        o = np.zeros((B, H, Lq, d))
+        lse = np.full((B, H, Lq), -np.inf)
+        for h in range(H):
+            S = q[0, h] @ k[0, h].T
+            if softcap > 0:
+                if kind == "softcap_before_scale":
+                    S = scale * softcap * np.tanh(S / softcap)
+                elif kind == "softcap_clamp":
+                    S = np.clip(scale * S, -softcap, softcap)
+                else:
+                    S = softcap * np.tanh(scale * S / softcap)
+            else:
+                S = scale * S
+            if alibi_slopes is not None:
+                hh = H - 1 - h if kind == "slopes_reversed" else h
+                rel = (j - np.arange(Lq)[:, None]) if kind == "alibi_top_left" else (j - pos)
+                S = S + (-1 if kind == "alibi_sign" else 1) * float(alibi_slopes[hh]) * rel
+            S = np.where(vis, S, -np.inf)
+            m = S.max(axis=1)
+            live = np.isfinite(m)
+            m0 = np.where(live, m, 0.0)
+            E = np.exp(S - m0[:, None])
+            l = np.where(live, E.sum(axis=1), 1.0)
+            o[0, h] = np.where(live[:, None], (E / l[:, None]) @ v[0, h], 0.0)
+            lse[0, h] = np.where(live, m0 + np.log(l), -np.inf)
+        return o, lse
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["softcap_before_scale", "softcap_clamp", "alibi_sign", "alibi_top_left",
+                                  "slopes_reversed", "window_off_by_one"])
+def test_score_mod_mutants_are_caught(kind):
+    fn = _mod_mutant(kind)
+    with np.errstate(all="ignore"):
+        assert not (pin_mod_bruteforce(fn) and pin_mod_reductions(fn) and pin_mod_closed_forms(fn))
+    none = _mod_mutant("none")
+    assert pin_mod_bruteforce(none) and pin_mod_reductions(none) and pin_mod_closed_forms(none)

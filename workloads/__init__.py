@@ -213,7 +213,19 @@ EXTENSION_CONFIGS = {
     "mla_decode": dict(name="shared_kv_decode_bf16_B64_Hq128_Hkv1_Lk32768_d128_s16", kind="decode_gqa",
                        dtype="bf16", B=64, Hq=128, Hkv=1, Lk=32768, d=128, scale=1.0 / math.sqrt(128),
                        num_splits=16, seed=9),
+    # Score modifications (the FlexAttention variants) on the causal prefill
+    # shape: one set of q, k, v for three variants, each on top of causal: an
+    # ALiBi bias with the geometric slopes, a tanh softcap of 50, and an
+    # element-level sliding window of 1024 keys.
+    "score_mod": dict(name="score_mod_bf16_B4_H32_L4096_d128", kind="attention", dtype="bf16", B=4, H=32,
+                      Lq=4096, Lk=4096, d=128, scale=1.0 / math.sqrt(128), causal=True, softcap=50.0,
+                      window=1024, seed=10),
 }
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """The geometric ALiBi slopes 2^(-8 (h + 1) / H), h = 0 .. H - 1 (float32)."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
 
 
 def gqa_inputs(cfg: dict, Lk: int | None = None):
