@@ -14,7 +14,9 @@ Extension workloads: element bitmaps in partial tiles (B2 H16 L8192 d64,
 TFLOP/s), row layer normalisation (fp32 4096 x 32768, GB/s), and decode with
 grouped queries at Lk 32768, d 128: 8 query heads per key/value head (B64 Hq64
 Hkv8, 4 splits) and 128 query heads on one cache (B64 Hq128 Hkv1, 16 splits),
-in GB/s with TFLOP/s alongside.
+in GB/s with TFLOP/s alongside; and the score modifications on the causal
+prefill shape (B4 H32 L4096 d128): ALiBi bias, tanh softcap 50, and a
+1024-key sliding window (TFLOP/s).
 
 Timing: inputs are resident in HBM before the timed region; W untimed
 warm-up calls; then K calls, each bracketed by HIP events recorded on the
@@ -47,6 +49,7 @@ KERNEL_SOURCES = {
     "copy": None, "softmax": "softmax_rows.hip", "prefill": "attention_bf16.hip", "decode": "decode_splitkv.hip",
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip", "bitmap": "attention_bf16.hip",
     "layernorm": "layernorm_rows.hip", "gqa": "attention_bf16.hip", "mla": "attention_bf16.hip",
+    "alibi": "attention_bf16.hip", "softcap": "attention_bf16.hip", "window": "attention_bf16.hip",
 }
 
 
@@ -134,6 +137,37 @@ def setup_prefill(rf, torch, W):
     flops = 4 * c["B"] * c["H"] * c["Lq"] * c["Lk"] * c["d"] / 2   # causal: half of the dense score matrix
     return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], causal=True, out=o, lse=lse),
                 work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, o, lse), cfg=c)
+
+
+def _setup_score_mod(rf, torch, W, kind):
+    c = W.EXTENSION_CONFIGS["score_mod"]
+    B, H, L, d = c["B"], c["H"], c["Lq"], c["d"]
+    q, k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, B, H, L, d, "bf16").view(np.int16))
+               .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    kw = {"alibi": dict(alibi_slopes=torch.from_numpy(W.alibi_slopes(H)).cuda()),
+          "softcap": dict(softcap=c["softcap"]), "window": dict(window=c["window"])}[kind]
+    if kind == "window":   # visible (row, key) pairs of a causal window, 4 d flop each
+        Wn = c["window"]
+        pairs = Wn * (Wn + 1) // 2 + (L - Wn) * Wn
+    else:                  # the causal convention of the prefill workload
+        pairs = L * L / 2
+    cfg = dict(c, name=f"{kind}_causal_bf16_B{B}_H{H}_L{L}_d{d}")
+    return dict(fn=lambda: rf.rf_attention_fwd_mod(q, k, v, scale=c["scale"], causal=True, out=o, lse=lse, **kw),
+                work=4 * B * H * pairs * d, unit="TFLOP/s", bound="mfma", keep=(q, k, v, o, lse, kw), cfg=cfg)
+
+
+def setup_alibi(rf, torch, W):
+    return _setup_score_mod(rf, torch, W, "alibi")
+
+
+def setup_softcap(rf, torch, W):
+    return _setup_score_mod(rf, torch, W, "softcap")
+
+
+def setup_window(rf, torch, W):
+    return _setup_score_mod(rf, torch, W, "window")
 
 
 def setup_sparse(rf, torch, W):
@@ -284,6 +318,7 @@ def setup_copy(rf, torch, W):
 
 
 SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse, "gqa": setup_gqa_decode, "mla": setup_mla_decode,
+          "alibi": setup_alibi, "softcap": setup_softcap, "window": setup_window,
           "attn_f32": setup_attn_f32}
 
 
@@ -321,7 +356,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla")
+    ap.add_argument("--workloads",
+                    default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -155,6 +155,32 @@ int rf_attention_fwd_bitmap(const void* q, const void* k, const void* v, void* o
                             const uint64_t* tile_bits, int dtype, void* stream);
 
 /*
+ * Attention with score modifications: rf_attention_fwd with, per head h,
+ * query row i at position p_i = i + Lk - Lq (bottom-right, as the causal
+ * rule) and key j,
+ *   s = scale * (q_i . k_j);
+ *   softcap > 0         : s <- softcap * tanh(s / softcap);
+ *   alibi_slopes != NULL: s <- s + alibi_slopes[h] * (j - p_i);
+ *   window > 0          : key j is visible only if j > p_i - window
+ *                         (with causal = 1: the window keys up to the row's own);
+ * then the masked softmax of rf_attention_fwd (causal rule and block mask
+ * apply as there). A row with no visible key gives O = 0, LSE = -inf.
+ * Source: FLASHLIGHT page, Risultati (the FlexAttention variants ALiBi,
+ * Softcap, Causal and Sliding Window; Softcap attention in LLaMa-3.2-1B).
+ *   window       : >= 0, 0 = no window.
+ *   alibi_slopes : fp32 [H] device pointer (natural-log units per position) or
+ *                  NULL for no bias; slopes may have any sign.
+ *   softcap      : finite, >= 0, 0 = no softcap.
+ * Tiles wholly before every row's window are neither loaded nor computed.
+ * Supported sizes and errors as rf_attention_fwd, plus RF_ERR_INVALID_ARG for
+ * window < 0, a negative or non-finite softcap, or misaligned alibi_slopes.
+ */
+int rf_attention_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                         const uint8_t* block_mask, int window, const float* alibi_slopes, float softcap,
+                         int dtype, void* stream);
+
+/*
  * Bytes of device workspace that rf_attention_decode_splitkv needs:
  * B*H*num_splits*(d + 1) fp32 values (normalised partial outputs and their
  * LSE), rounded up to 256 bytes. Returns 0 for invalid arguments.
@@ -253,7 +279,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 3
+#define RF_ABI_VERSION 4
 int rf_abi_version(void);
 
 #ifdef __cplusplus

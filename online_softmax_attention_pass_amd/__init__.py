@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "RF_F32", "RF_BF16", "RFError", "load", "library_path",
-    "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_decode_splitkv",
+    "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_fwd_mod",
+    "rf_attention_decode_splitkv",
     "rf_attention_decode_splitkv_workspace_size", "rf_attention_decode_gqa", "rf_attention_decode_gqa_workspace_size",
     "rf_lse_merge", "rf_abi_version",
 ]
@@ -55,6 +56,7 @@ def load():
         "rf_layernorm_rows": ([P, P, P, P, P, P, I64, I64, F, I, P], I),
         "rf_attention_fwd": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P], I),
         "rf_attention_fwd_bitmap": ([P, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P], I),
+        "rf_attention_fwd_mod": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, F, I, P], I),
         "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_splitkv": ([P, P, P, P, P, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_attention_decode_gqa_workspace_size": ([I, I, I, I], SZ),
@@ -198,6 +200,41 @@ def rf_attention_fwd(q, k, v, scale=None, causal=False, block_mask=None, out=Non
     st = lib.rf_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
                               1 if causal else 0, _ptr(block_mask), _dtype_code(q), _stream(dev))
     _check(st, "rf_attention_fwd")
+    return o, lse
+
+
+def rf_attention_fwd_mod(q, k, v, scale=None, causal=False, block_mask=None, window=0, alibi_slopes=None, softcap=0.0,
+                         out=None, lse=None, want_lse=True):
+    """Attention with score modifications: softcap (tanh), ALiBi bias (alibi_slopes fp32 [H] on the GPU),
+    element-level sliding window of `window` keys. Shapes and outputs as rf_attention_fwd."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if block_mask is not None:
+        want = (math.ceil(Lq / MASK_TILE), math.ceil(Lk / MASK_TILE))
+        if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != want:
+            raise ValueError(f"block_mask must be uint8 {want}")
+    if alibi_slopes is not None and (alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (H,)):
+        raise ValueError(f"alibi_slopes must be fp32 [{H}]")
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    dev = _dev(q, k, v, o, lse, block_mask, alibi_slopes)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.rf_attention_fwd_mod(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
+                                  1 if causal else 0, _ptr(block_mask), int(window), _ptr(alibi_slopes),
+                                  float(softcap), _dtype_code(q), _stream(dev))
+    _check(st, "rf_attention_fwd_mod")
     return o, lse
 
 

@@ -147,6 +147,19 @@ __device__ __forceinline__ void publish_lds_loads() {
   __syncthreads();
 }
 
+// Score modifications of one call. The MOD kernel instance turns each score
+// tile into log2-unit scores t = scale log2(e) (q . k) and then applies, in this
+// order, a softcap t <- cap2 tanh(t / cap2) (cap2 = softcap log2 e, the natural
+// softcap moved to log2 units) and an ALiBi bias t <- t + slope_h log2(e)
+// (j - p_i), p_i = i + Lk - Lq; a window keeps keys j > p_i - window.
+struct ScoreMod {
+  const float* slopes = nullptr;  // ALiBi slope per head (natural units per position), or none
+  int H = 1;                      // heads: the slope of item head bh is slopes[bh % H]
+  float cap2 = 0.f;               // softcap in log2 units, 0 = none
+  float tk = 0.f;                 // 2 log2(e) / cap2: tanh(y) = 1 - 2 / (1 + 2^(t tk)), y = t / cap2
+  int window = 0;                 // keys per row window, 0 = none
+};
+
 // Walks the key tiles a workgroup must visit, in order. Without a block mask it
 // is every tile below kt_end. With one, the mask bytes of the next 64 tiles are
 // read once per 64 tiles (one byte per lane) and turned into two wave-uniform
@@ -296,13 +309,16 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 // ws_lse [head rows, n_splits] for a log-sum-exp merge. Used for decode with
 // grouped queries, where the query heads sharing one key/value head are the
 // rows of the query tile.
-template <int D, int NW, int WPE, bool BITS, bool SPLIT = false>
+//
+// MOD: score modifications (ScoreMod) applied to each score tile before the mask.
+template <int D, int NW, int WPE, bool BITS, bool SPLIT = false, bool MOD = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
     const uint8_t* __restrict__ block_mask, int n_qt, int64_t n_items, int xcd_remap, int head_group,
     int64_t item_base, const uint64_t* __restrict__ tile_bits, uint32_t bits_bytes, int n_splits = 1,
-    int kt_split = 0, float* __restrict__ ws_o = nullptr, float* __restrict__ ws_lse = nullptr) {
+    int kt_split = 0, float* __restrict__ ws_o = nullptr, float* __restrict__ ws_lse = nullptr,
+    ScoreMod mod = ScoreMod{}) {
   constexpr int BN = 64;
   constexpr int BM = 32 * NW;
   constexpr int KCH = D / 8;
@@ -365,7 +381,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
     if (last_key > Lk - 1) last_key = Lk - 1;
     const int kt_all = last_key < 0 ? 0 : int(last_key / BN) + 1;
-    const int kt_begin = SPLIT ? split * kt_split : 0;
+    // With a window, tiles wholly before the first row's lowest key are skipped.
+    const int64_t lo_first = int64_t(q0) + off - mod.window + 1;
+    const int kt_begin = SPLIT ? split * kt_split : ((MOD && mod.window > 0 && lo_first > 0) ? int(lo_first / BN) : 0);
     const int kt_end = SPLIT ? min(kt_all, kt_begin + kt_split) : kt_all;
     TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
                     min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
@@ -393,6 +411,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     float m_ref = kNegInf, l_run = 0.f, l_rnd = 0.f;
     const int64_t row_last = causal ? int64_t(q0w + l32) + off : int64_t(Lk) - 1;
     const int row_lim = int(row_last < int64_t(Lk) - 1 ? (row_last < -1 ? -1 : row_last) : int64_t(Lk) - 1);
+    // Score modifications: scores become log2-unit t before the exponentials,
+    // which then take them as they are.
+    const float c_exp = MOD ? 1.f : c_log2;
+    // This lane's query position (below 2^31: the boundary bounds Lk d 2 by 2^31).
+    const int qpos = q0w + l32 + int(off);
+    const float sl2 = (MOD && mod.slopes != nullptr) ? mod.slopes[bh % mod.H] * kLog2e : 0.f;
+    // Window: this row's lowest visible key, and the largest such bound in the
+    // wave (tiles starting below it need the element mask).
+    const int64_t lo_row = int64_t(qpos) - mod.window + 1;
+    const int row_lo = (MOD && mod.window > 0) ? int(lo_row < 0 ? 0 : (lo_row > Lk ? Lk : lo_row)) : 0;
+    const int64_t lo_wave = int64_t(q0w + 31) + off - mod.window + 1;
 
     // ---- stage pieces (inlined into the phase bodies below) ----
     auto score_mfmas = [&](const uint16_t* ks_, f32x16_t (&sacc)[MB]) {
@@ -426,8 +455,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(st[mb][r], c_log2, -mu));
-          const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_log2, -mu));
+          const float p0 = fast_exp2(fmaf(st[mb][r], c_exp, -mu));
+          const float p1 = fast_exp2(fmaf(st[mb][r + 1], c_exp, -mu));
           const uint32_t pp = cvt_pk_bf16(p0, p1);
           lt += p0 + p1;
           ltr = add_bf16_pair(pp, ltr);
@@ -473,18 +502,41 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     auto row_word = [&](int part, const uint64_t* bb) -> uint64_t {
       return (BITS && (part & 1)) ? bb[32 * wave + l32] : ~uint64_t(0);
     };
-    auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine, int part, uint64_t word) {
-      const int k0 = kt * BN;
-      const bool bitmap = BITS && (part & 1);
-      const bool edge =
-          !mine || bitmap || (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
-      if (edge) {
-        const int lim = mine ? row_lim - k0 - 4 * h : -BN;
+    // Score modifications of a fresh score tile (before its mask): t = c S,
+    // then the softcap, then the ALiBi bias. Lane (row l32, half h) holds key
+    // k0 + 4 h + 32 mb + 8 (r / 4) + r % 4 in st[mb][r].
+    auto mod_tile = [&](f32x16_t (&st)[MB], int kt) {
+      if constexpr (MOD) {
+        const float base = sl2 * float(kt * BN + 4 * h - qpos);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * mb + 8 * (r >> 2) + (r & 3) > lim) st[mb][r] = kNegInf;
+          for (int r = 0; r < 16; ++r) {
+            float t = st[mb][r] * c_log2;
+            if (mod.cap2 > 0.f) {
+              const float e = fast_exp2(t * mod.tk);
+              t = fmaf(-2.f * mod.cap2, __builtin_amdgcn_rcpf(1.f + e), mod.cap2);
+            }
+            st[mb][r] = fmaf(sl2, float(32 * mb + 8 * (r >> 2) + (r & 3)), t + base);
+          }
+      }
+    };
+    auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine, int part, uint64_t word) {
+      const int k0 = kt * BN;
+      const bool bitmap = BITS && (part & 1);
+      const bool below_window = MOD && mod.window > 0 && int64_t(k0) < lo_wave;
+      const bool edge = !mine || bitmap || below_window ||
+                        (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
+      if (edge) {
+        const int lim = mine ? row_lim - k0 - 4 * h : -BN;
+        const int lo = row_lo - k0 - 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int idx = 32 * mb + 8 * (r >> 2) + (r & 3);
+            if (idx > lim || (MOD && idx < lo)) st[mb][r] = kNegInf;
+          }
         if (bitmap) {
           // Key 32 mb + 8 (r / 4) + 4 h + r % 4 of the tile is visible iff its
           // bit in this row's word is set.
@@ -507,7 +559,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
       mx = pair_max_halves(mx);
-      const float mt = mx * c_log2;
+      const float mt = mx * c_exp;
       const bool move = mt > m_ref + kRescaleSlack;
       *moved = __builtin_amdgcn_ballot_w64(move) != 0;
       float alpha = 1.f;
@@ -551,8 +603,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // One score pair (keys 2r, 2r + 1 of 32-key block mb) of P against mu.
     auto exp_pair = [&](const f32x16_t (&st)[MB], uint32_t (&pk)[MB][8], int mb, int r, float mu, float& lt,
                         float& ltr) {
-      const float p0 = fast_exp2(fmaf(st[mb][2 * r], c_log2, -mu));
-      const float p1 = fast_exp2(fmaf(st[mb][2 * r + 1], c_log2, -mu));
+      const float p0 = fast_exp2(fmaf(st[mb][2 * r], c_exp, -mu));
+      const float p1 = fast_exp2(fmaf(st[mb][2 * r + 1], c_exp, -mu));
       const uint32_t pp = cvt_pk_bf16(p0, p1);
       lt += p0 + p1;
       ltr = add_bf16_pair(pp, ltr);
@@ -624,6 +676,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[0][i]));
       asm volatile("" ::"v"(lt0), "v"(ltr0));
       commit_half(s_cur, pk, 0, lt0, ltr0);
+      mod_tile(s_next, kt_next);
       mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       {
         const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
@@ -683,8 +736,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
             const int pr = i * PPC + j;
             if (pr < PAIRS) {
               const int cb = pr / 8, r = 2 * (pr % 8);
-              const float p0 = fast_exp2(fmaf(s_cur[cb][r], c_log2, -mu));
-              const float p1 = fast_exp2(fmaf(s_cur[cb][r + 1], c_log2, -mu));
+              const float p0 = fast_exp2(fmaf(s_cur[cb][r], c_exp, -mu));
+              const float p1 = fast_exp2(fmaf(s_cur[cb][r + 1], c_exp, -mu));
               const uint32_t pp = cvt_pk_bf16(p0, p1);
               lt += p0 + p1;
               ltr = add_bf16_pair(pp, ltr);
@@ -705,12 +758,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       asm volatile("" ::"v"(lt), "v"(ltr));
 #if RF_ATT_SUMGUARD
       commit_tile(s_cur, pk, lt, ltr);
+      mod_tile(s_next, kt_next);
       mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       // Phase B: P.V product of this tile.
       pv_mfmas(vs_cur, pk);
 #else
       l_run += lt;
       l_rnd += ltr;
+      mod_tile(s_next, kt_next);
       mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
       // Phase B: P.V product of this tile with the row maximum of the next one.
       pv_mfmas(vs_cur, pk);
@@ -771,6 +826,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
       publish_lds_loads();  // K(t0), K(t1), V(t0) resident
       score_mfmas(kb0, s0);
+      mod_tile(s0, t0);
       mask_tile(s0, t0, m0, p0, row_word(p0, bb0));
       {
         bool moved = false;
@@ -891,10 +947,10 @@ inline float score_coef(float scale, int* q_mode) {
 
 // One workgroup per item (b, h, query tile); more items than one grid allows go
 // in chunks (then without the XCD placement, which assumes the whole item range).
-template <int D, int NW, int WPE, bool BITS>
+template <int D, int NW, int WPE, bool BITS, bool MOD = false>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
                      float scale, int causal, const uint8_t* block_mask, const uint64_t* tile_bits,
-                     hipStream_t stream) {
+                     hipStream_t stream, ScoreMod mod = ScoreMod{}) {
   constexpr int BM = 32 * NW;
   const int n_qt = (Lq + BM - 1) / BM;
   const int64_t n_items = int64_t(B) * H * n_qt;
@@ -907,11 +963,11 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
       BITS ? uint32_t(int64_t((Lq + kMaskTile - 1) / kMaskTile) * ((Lk + kMaskTile - 1) / kMaskTile) * 512) : 0u;
   for (int64_t base = 0; base < n_items; base += cap) {
     const int64_t n = n_items - base < cap ? n_items - base : cap;
-    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS>), dim3(unsigned(n)), dim3(NW * 64), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS, false, MOD>), dim3(unsigned(n)), dim3(NW * 64),
+                       0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
                        block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base,
-                       tile_bits, bits_bytes);
+                       tile_bits, bits_bytes, 1, 0, nullptr, nullptr, mod);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -958,7 +1014,21 @@ hipError_t launch_attention_bf16_split(const void* q, const void* k, const void*
 
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                  int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
-                                 const uint64_t* tile_bits, hipStream_t stream) {
+                                 const uint64_t* tile_bits, hipStream_t stream, int window,
+                                 const float* alibi_slopes, float softcap) {
+  if (window > 0 || alibi_slopes != nullptr || softcap > 0.f) {  // score modifications
+    ScoreMod m;
+    m.slopes = alibi_slopes;
+    m.H = H;
+    m.cap2 = softcap > 0.f ? float(double(softcap) * 1.4426950408889634) : 0.f;
+    m.tk = softcap > 0.f ? float(2.0 / double(softcap)) : 0.f;
+    m.window = window;
+    if (d == 128)
+      return launch_sp<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, false, true>(q, k, v, o, lse, B, H, Lq, Lk, scale,
+                                                                         causal, block_mask, nullptr, stream, m);
+    return launch_sp<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, false, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
+                                                                    block_mask, nullptr, stream, m);
+  }
   if (tile_bits != nullptr) {  // element bitmaps inside partial tiles
     if (d == 128)
       return launch_sp<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,

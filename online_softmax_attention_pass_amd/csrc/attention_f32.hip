@@ -32,7 +32,8 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
                                                             float scale_log2, int causal,
                                                             const uint8_t* __restrict__ block_mask,
                                                             const uint64_t* __restrict__ tile_bits, int n_qt,
-                                                            int64_t n_items) {
+                                                            int64_t n_items, int window,
+                                                            const float* __restrict__ slopes, float softcap) {
   // Rows padded by 4 floats: 16-byte aligned, and the 16 key rows one
   // instruction reads start 4 banks apart.
   constexpr int DP = DMAX + 4;
@@ -64,6 +65,12 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
     }
 
     const int qi = q0 + r;  // this lane's query row
+    // Score modifications: query position (bottom-right), the head's ALiBi
+    // slope in log2 units, and the window's lowest key for this row.
+    const int64_t qpos = int64_t(qi) + (Lk - Lq);
+    const float sl2 = slopes != nullptr ? slopes[bh % H] * kLog2e : 0.f;
+    const int64_t lo = window > 0 ? qpos - window + 1 : 0;
+    const int64_t lo_first = int64_t(q0) + (Lk - Lq) - window + 1;  // lowest window key of the tile's rows
     float m = kNegInf, l = 0.f;
     float acc[NC];
 #pragma unroll
@@ -74,6 +81,7 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
     for (int kt = 0; kt < n_kt; ++kt) {
       const int k0 = kt * kBN;
       if (causal && k0 > causal_last) break;  // every later tile is masked too
+      if (window > 0 && int64_t(k0) + kBN - 1 < lo_first) continue;  // before every row's window
       const int64_t tile = int64_t(q0 / kMaskTile) * n_mask_cols + k0 / kMaskTile;
       const uint8_t kind = block_mask != nullptr ? block_mask[tile] : uint8_t(1);
       if (kind == 0) continue;  // the whole tile is masked: skip it, no load
@@ -115,8 +123,14 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
       for (int j = 0; j < 2; ++j) {
         const int kj = k0 + p + 16 * j;
         const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= int64_t(qi) + (Lk - Lq)) &&
-                         ((word >> (kj % kMaskTile)) & 1);
-        s[j] = vis ? dots[j] * scale_log2 : kNegInf;
+                         ((word >> (kj % kMaskTile)) & 1) && int64_t(kj) >= lo;
+        // s = scale (q . k) in log2 units; the softcap cap tanh(s / cap) moves
+        // to log2 units as (cap log2 e) tanh(t / (cap log2 e)); ALiBi adds
+        // slope (j - p_i).
+        float t2 = dots[j] * scale_log2;
+        if (softcap > 0.f) t2 = softcap * kLog2e * tanhf(t2 / (softcap * kLog2e));
+        t2 = fmaf(sl2, float(int64_t(kj) - qpos), t2);
+        s[j] = vis ? t2 : kNegInf;
         bm = fmaxf(bm, s[j]);
       }
       bm = group_max<16>(bm);
@@ -170,14 +184,16 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
 
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
                                 int H, int Lq, int Lk, int d, float scale, int causal,
-                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream) {
+                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream,
+                                int window, const float* alibi_slopes, float softcap) {
   const int n_qt = (Lq + kBM - 1) / kBM;
   const int64_t n_items = int64_t(B) * H * n_qt;
   const unsigned grid = unsigned(n_items < (1LL << 20) ? n_items : (1LL << 20));
   const float scale_log2 = float(double(scale) * 1.4426950408889634);
 #define RF_ATT_F32(DM)                                                                                    \
   hipLaunchKernelGGL((attention_f32_kernel<DM>), dim3(grid), dim3(256), 0, stream, q, k, v, o, lse, H, Lq, \
-                     Lk, d, scale_log2, causal, block_mask, tile_bits, n_qt, n_items)
+                     Lk, d, scale_log2, causal, block_mask, tile_bits, n_qt, n_items, window, alibi_slopes, \
+                     softcap)
   if (d <= 32)
     RF_ATT_F32(32);
   else if (d <= 64)

@@ -141,7 +141,8 @@ namespace {
 // Shared body of the two attention entry points; `name` labels the errors.
 int attention_common(const char* name, const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int H, int Lq, int Lk, int d, float scale, int causal, const uint8_t* block_mask,
-                     const uint64_t* tile_bits, int dtype, void* stream) {
+                     const uint64_t* tile_bits, int dtype, void* stream, int window = 0,
+                     const float* alibi_slopes = nullptr, float softcap = 0.f) {
   try {
     if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
     if (B < 0 || H < 0 || Lq < 0 || Lk < 0)
@@ -179,14 +180,17 @@ int attention_common(const char* name, const void* q, const void* k, const void*
       return fail(RF_ERR_INVALID_ARG, "%s: fp32 tensors must be 4-byte aligned", name);
     }
     if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "%s: lse misaligned", name);
+    if (alibi_slopes != nullptr && !aligned(alibi_slopes, 4))
+      return fail(RF_ERR_INVALID_ARG, "%s: alibi_slopes misaligned", name);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e =
         dtype == RF_BF16
             ? rf::launch_attention_bf16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, block_mask, tile_bits,
-                                        s)
+                                        s, window, alibi_slopes, softcap)
             : rf::launch_attention_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                                        static_cast<const float*>(v), static_cast<float*>(o), lse, B, H, Lq, Lk,
-                                       d, scale, causal != 0, block_mask, tile_bits, s);
+                                       d, scale, causal != 0, block_mask, tile_bits, s, window, alibi_slopes,
+                                       softcap);
     return hip_status(e, name);
   } catch (const std::exception& e) {
     return fail(RF_ERR_HIP, "%s: %s", name, e.what());
@@ -209,6 +213,17 @@ int rf_attention_fwd_bitmap(const void* q, const void* k, const void* v, void* o
     return fail(RF_ERR_INVALID_ARG, "rf_attention_fwd_bitmap: NULL tile_bits");
   return attention_common("rf_attention_fwd_bitmap", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, tile_kind,
                           tile_bits, dtype, stream);
+}
+
+int rf_attention_fwd_mod(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq,
+                         int Lk, int d, float scale, int causal, const uint8_t* block_mask, int window,
+                         const float* alibi_slopes, float softcap, int dtype, void* stream) {
+  const char* name = "rf_attention_fwd_mod";
+  if (window < 0) return fail(RF_ERR_INVALID_ARG, "%s: window = %d < 0", name, window);
+  if (!std::isfinite(softcap) || softcap < 0.f)
+    return fail(RF_ERR_INVALID_ARG, "%s: softcap must be finite and >= 0", name);
+  return attention_common(name, q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, block_mask, nullptr, dtype, stream,
+                          window, alibi_slopes, softcap);
 }
 
 size_t rf_attention_decode_splitkv_workspace_size(int B, int H, int d, int num_splits) {

@@ -135,14 +135,19 @@ hipError_t launch_decode_partials(const void* q, const void* k, const void* v, f
 // bitmaps, used where the kind is neither 0 nor 1.
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                                 int B, int H, int Lq, int Lk, int d, float scale, int causal,
-                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream);
+                                const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream,
+                                int window = 0, const float* alibi_slopes = nullptr, float softcap = 0.f);
 // Split-KV partials of the pipelined bf16 kernel (no mask): n_heads heads of
 // Lq query rows, fp32 normalised partials into ws_o [n_heads * Lq, n_splits, d]
 // and ws_lse [n_heads * Lq, n_splits].
 hipError_t launch_attention_bf16_split(const void* q, const void* k, const void* v, float* ws_o, float* ws_lse,
                                        int n_heads, int Lq, int Lk, int d, float scale, int n_splits,
                                        hipStream_t stream);
+// Score modifications (window > 0, alibi_slopes [H] device pointer, softcap > 0)
+// select the instance that applies them; tile_bits is then ignored (the entry
+// point with modifications takes no bitmaps).
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int H, int Lq, int Lk, int d, float scale, int causal,
-                                 const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream);
+                                 const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream,
+                                 int window = 0, const float* alibi_slopes = nullptr, float softcap = 0.f);
 }  // namespace rf

@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 3
+    assert lib.rf_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -128,6 +128,26 @@ def test_attention_validation(lib, kw, code):
     assert att(lib, **kw) == code
     if code != OK:
         assert "rf_attention_fwd" in _msg(lib)
+
+
+def att_mod(lib, **kw):
+    a = dict(ATT, window=0, slopes=NUL, cap=0.0)
+    a.update(kw)
+    return lib.rf_attention_fwd_mod(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"],
+                                    a["d"], a["scale"], a["causal"], a["mask"], a["window"], a["slopes"], a["cap"],
+                                    a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), INVALID), (dict(cap=-1.0), INVALID), (dict(cap=float("nan")), INVALID),
+    (dict(cap=float("inf")), INVALID), (dict(slopes=P(0x10002)), INVALID),
+    (dict(dtype=7), INVALID), (dict(d=96), UNSUP), (dict(q=NUL), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(B=0, window=16, cap=30.0), OK), (dict(Lq=0, slopes=FAKE), OK),
+])
+def test_attention_mod_validation(lib, kw, code):
+    assert att_mod(lib, **kw) == code
+    if code != OK:
+        assert "rf_attention_fwd_mod" in _msg(lib)
 
 
 def att_bitmap(lib, **kw):
