@@ -158,6 +158,7 @@ struct ScoreMod {
   float cap2 = 0.f;               // softcap in log2 units, 0 = none
   float tk = 0.f;                 // 2 log2(e) / cap2: tanh(y) = 1 - 2 / (1 + 2^(t tk)), y = t / cap2
   int window = 0;                 // keys per row window, 0 = none
+  int rev = 0;                    // visit the key tiles last to first (no block mask only)
 };
 
 // Walks the key tiles a workgroup must visit, in order. Without a block mask it
@@ -310,8 +311,9 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 // grouped queries, where the query heads sharing one key/value head are the
 // rows of the query tile.
 //
-// MOD: score modifications (ScoreMod) applied to each score tile before the mask.
-template <int D, int NW, int WPE, bool BITS, bool SPLIT = false, bool MOD = false>
+// MOD: score modifications (ScoreMod) applied to each score tile before the mask;
+// 1 = bias and window, 2 = also the softcap.
+template <int D, int NW, int WPE, bool BITS, bool SPLIT = false, int MOD = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
@@ -423,6 +425,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int row_lo = (MOD && mod.window > 0) ? int(lo_row < 0 ? 0 : (lo_row > Lk ? Lk : lo_row)) : 0;
     const int64_t lo_wave = int64_t(q0w + 31) + off - mod.window + 1;
 
+    // Key tile of walk position t: the walk runs first to last; with rev the
+    // tiles are visited last to first (the diagonal first under an ALiBi
+    // bias, so the reference starts at the row's largest scores).
+    const bool rev = MOD && mod.rev != 0;
+    auto tile = [&](int t) { return rev ? kt_begin + kt_end - 1 - t : t; };
+
     // ---- stage pieces (inlined into the phase bodies below) ----
     auto score_mfmas = [&](const uint16_t* ks_, f32x16_t (&sacc)[MB]) {
 #pragma unroll
@@ -505,20 +513,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // Score modifications of a fresh score tile (before its mask): t = c S,
     // then the softcap, then the ALiBi bias. Lane (row l32, half h) holds key
     // k0 + 4 h + 32 mb + 8 (r / 4) + r % 4 in st[mb][r].
+    auto mod_base = [&](int kt) { return sl2 * float(kt * BN + 4 * h - qpos); };
+    auto mod_elem = [&](f32x16_t (&st)[MB], int mb, int r, float base) {
+      const float bias = fmaf(sl2, float(32 * mb + 8 * (r >> 2) + (r & 3)), base);
+      if constexpr (MOD == 2) {
+        float t = st[mb][r] * c_log2;
+        const float e = fast_exp2(t * mod.tk);
+        t = fmaf(-2.f * mod.cap2, __builtin_amdgcn_rcpf(1.f + e), mod.cap2);
+        st[mb][r] = t + bias;
+      } else {
+        st[mb][r] = fmaf(st[mb][r], c_log2, bias);
+      }
+    };
     auto mod_tile = [&](f32x16_t (&st)[MB], int kt) {
       if constexpr (MOD) {
-        const float base = sl2 * float(kt * BN + 4 * h - qpos);
+        const float base = mod_base(kt);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float t = st[mb][r] * c_log2;
-            if (mod.cap2 > 0.f) {
-              const float e = fast_exp2(t * mod.tk);
-              t = fmaf(-2.f * mod.cap2, __builtin_amdgcn_rcpf(1.f + e), mod.cap2);
-            }
-            st[mb][r] = fmaf(sl2, float(32 * mb + 8 * (r >> 2) + (r & 3)), t + base);
-          }
+          for (int r = 0; r < 16; ++r) mod_elem(st, mb, r, base);
       }
     };
     auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine, int part, uint64_t word) {
@@ -676,8 +689,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[0][i]));
       asm volatile("" ::"v"(lt0), "v"(ltr0));
       commit_half(s_cur, pk, 0, lt0, ltr0);
-      mod_tile(s_next, kt_next);
-      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
+      // With score modifications, d = 64 runs them (and then the mask) in the
+      // shadow of phase B2; d = 128 has no registers for the unmasked scores
+      // to live that long and runs them here.
+      constexpr bool MOD_IN_B2 = MOD != 0 && D <= 64;
+      if constexpr (!MOD_IN_B2) {
+        mod_tile(s_next, kt_next);
+        mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
+      }
       {
         const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
         constexpr int NB1 = NPV / 2;
@@ -693,7 +712,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[1][i]));
       asm volatile("" ::"v"(lt1), "v"(ltr1));
       commit_half(s_cur, pk, 1, lt1, ltr1);
-      pv_range(vs_cur, pk, NPV / 2, NPV, [](int) {});
+      if constexpr (MOD_IN_B2) {
+        // Phase B2 issues only matrix-core work: the next tile's score
+        // modifications run in its shadow, then its mask.
+        constexpr int NB2 = NPV - NPV / 2;
+        const float base = mod_base(kt_next);
+        pv_range(vs_cur, pk, NPV / 2, NPV, [&](int j) {
+#pragma unroll
+          for (int e = j * 16 * MB / NB2; e < (j + 1) * 16 * MB / NB2; ++e) mod_elem(s_next, e / 16, e % 16, base);
+#if RF_ATT_SP_SCHED
+          __builtin_amdgcn_sched_barrier(0);
+#endif
+        });
+        mask_tile(s_next, kt_next, mine_next, part_next, ~uint64_t(0));
+      } else {
+        pv_range(vs_cur, pk, NPV / 2, NPV, [](int) {});
+      }
     };
 #else
     // One steady-state step: current tile (scores s_cur, V in vs_cur), next tile
@@ -817,17 +851,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     int t0 = walk.next(kt_begin, &m0, &p0);
     if (t0 < kt_end) {
       int t1 = walk.next(t0 + 1, &m1, &p1);
-      dma_one(khead, head_bytes, kb0, uint32_t(t0) * BN * D * 2, kv_off, wave * IPW, IPW);
-      dma_one(vhead, head_bytes, vb0, uint32_t(t0) * BN * D * 2, vv_off, wave * IPW, IPW);
-      load_bits(bb0, t0, p0);
+      dma_one(khead, head_bytes, kb0, uint32_t(tile(t0)) * BN * D * 2, kv_off, wave * IPW, IPW);
+      dma_one(vhead, head_bytes, vb0, uint32_t(tile(t0)) * BN * D * 2, vv_off, wave * IPW, IPW);
+      load_bits(bb0, tile(t0), p0);
       if (t1 < kt_end) {
-        dma_one(khead, head_bytes, kb1, uint32_t(t1) * BN * D * 2, kv_off, wave * IPW, IPW);
-        load_bits(bb1, t1, p1);
+        dma_one(khead, head_bytes, kb1, uint32_t(tile(t1)) * BN * D * 2, kv_off, wave * IPW, IPW);
+        load_bits(bb1, tile(t1), p1);
       }
       publish_lds_loads();  // K(t0), K(t1), V(t0) resident
       score_mfmas(kb0, s0);
-      mod_tile(s0, t0);
-      mask_tile(s0, t0, m0, p0, row_word(p0, bb0));
+      mod_tile(s0, tile(t0));
+      mask_tile(s0, tile(t0), m0, p0, row_word(p0, bb0));
       {
         bool moved = false;
         const float alpha = tile_max(s0, &moved);
@@ -842,11 +876,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         if (t1 >= kt_end) break;
         int t2 = walk.next(t1 + 1, &m2, &p2);
         if (t2 < kt_end) {
-          dma_one(khead, head_bytes, kb0, uint32_t(t2) * BN * D * 2, kv_off, wave * IPW, IPW);
-          load_bits(bb0, t2, p2);
+          dma_one(khead, head_bytes, kb0, uint32_t(tile(t2)) * BN * D * 2, kv_off, wave * IPW, IPW);
+          load_bits(bb0, tile(t2), p2);
         }
-        dma_one(vhead, head_bytes, vb1, uint32_t(t1) * BN * D * 2, vv_off, wave * IPW, IPW);
-        step(kb1, vb0, s0, s1, t1, m1, p1, bb1);
+        dma_one(vhead, head_bytes, vb1, uint32_t(tile(t1)) * BN * D * 2, vv_off, wave * IPW, IPW);
+        step(kb1, vb0, s0, s1, tile(t1), m1, p1, bb1);
 
         publish_lds_loads();  // this step's loads resident; kb1 and vb0 free
         if (t2 >= kt_end) {
@@ -859,11 +893,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         int p3 = 0;
         const int t3 = walk.next(t2 + 1, &m3, &p3);
         if (t3 < kt_end) {
-          dma_one(khead, head_bytes, kb1, uint32_t(t3) * BN * D * 2, kv_off, wave * IPW, IPW);
-          load_bits(bb1, t3, p3);
+          dma_one(khead, head_bytes, kb1, uint32_t(tile(t3)) * BN * D * 2, kv_off, wave * IPW, IPW);
+          load_bits(bb1, tile(t3), p3);
         }
-        dma_one(vhead, head_bytes, vb0, uint32_t(t2) * BN * D * 2, vv_off, wave * IPW, IPW);
-        step(kb0, vb1, s1, s0, t2, m2, p2, bb0);
+        dma_one(vhead, head_bytes, vb0, uint32_t(tile(t2)) * BN * D * 2, vv_off, wave * IPW, IPW);
+        step(kb0, vb1, s1, s0, tile(t2), m2, p2, bb0);
         t1 = t3;
         m1 = m3;
         p1 = p3;
@@ -947,7 +981,7 @@ inline float score_coef(float scale, int* q_mode) {
 
 // One workgroup per item (b, h, query tile); more items than one grid allows go
 // in chunks (then without the XCD placement, which assumes the whole item range).
-template <int D, int NW, int WPE, bool BITS, bool MOD = false>
+template <int D, int NW, int WPE, bool BITS, int MOD = 0>
 hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
                      float scale, int causal, const uint8_t* block_mask, const uint64_t* tile_bits,
                      hipStream_t stream, ScoreMod mod = ScoreMod{}) {
@@ -1023,11 +1057,22 @@ hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, vo
     m.cap2 = softcap > 0.f ? float(double(softcap) * 1.4426950408889634) : 0.f;
     m.tk = softcap > 0.f ? float(2.0 / double(softcap)) : 0.f;
     m.window = window;
+    // ALiBi slopes are positive by convention, so a row's scores grow toward its
+    // own position: walk from the diagonal back (the visiting order changes no
+    // result, only how often the lazy reference moves).
+    m.rev = (alibi_slopes != nullptr && block_mask == nullptr) ? 1 : 0;
+    if (softcap > 0.f) {
+      if (d == 128)
+        return launch_sp<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, false, 2>(q, k, v, o, lse, B, H, Lq, Lk, scale,
+                                                                        causal, block_mask, nullptr, stream, m);
+      return launch_sp<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, false, 2>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
+                                                                   block_mask, nullptr, stream, m);
+    }
     if (d == 128)
-      return launch_sp<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, false, true>(q, k, v, o, lse, B, H, Lq, Lk, scale,
-                                                                         causal, block_mask, nullptr, stream, m);
-    return launch_sp<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, false, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
-                                                                    block_mask, nullptr, stream, m);
+      return launch_sp<128, RF_ATT_NW_D128, RF_ATT_WPE_D128, false, 1>(q, k, v, o, lse, B, H, Lq, Lk, scale,
+                                                                      causal, block_mask, nullptr, stream, m);
+    return launch_sp<64, RF_ATT_NW_D64, RF_ATT_WPE_D64, false, 1>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal,
+                                                                 block_mask, nullptr, stream, m);
   }
   if (tile_bits != nullptr) {  // element bitmaps inside partial tiles
     if (d == 128)
