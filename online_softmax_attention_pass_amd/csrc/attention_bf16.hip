@@ -62,23 +62,11 @@ namespace {
 #ifndef RF_ATT_VREAD_AHEAD
 #define RF_ATT_VREAD_AHEAD 2
 #endif
-#ifndef RF_ATT_SPLITEXP
-#define RF_ATT_SPLITEXP 1
-#endif
-#ifndef RF_ATT_SUMGUARD
-#define RF_ATT_SUMGUARD 1
-#endif
-#if RF_ATT_SPLITEXP && !RF_ATT_SUMGUARD
-#error "the split exponentials rely on the sum guard"
-#endif
 #ifndef RF_ATT_HEAD_GROUP
 #define RF_ATT_HEAD_GROUP 2
 #endif
 #ifndef RF_ATT_SP_SCHED
 #define RF_ATT_SP_SCHED 1
-#endif
-#ifndef RF_ATT_SP_VALU_B
-#define RF_ATT_SP_VALU_B 2
 #endif
 #ifndef RF_ATT_WPE_D64
 #define RF_ATT_WPE_D64 2
@@ -280,28 +268,28 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Software-pipelined variant of the direct-to-LDS kernel.
+// Software-pipelined attention kernel.
 //
 // Within one wave the three stages of a key tile (score product, softmax
 // update, P.V product) depend on each other, so run back to back they leave
 // the matrix core idle during the exponentials and the vector ALU idle during
-// the products. Here every wave runs them one tile apart:
+// the products. Here every wave runs them one tile apart, in three phases per
+// step (tile j current, tile j+1 next):
 //
-//   phase A of tile j :  S(j+1) = K(j+1) Q^T      while  P(j) = exp(S(j) - m)
-//   phase B of tile j :  O^T   += V(j)^T P(j)^T   while  m <- max(m, rowmax S(j+1))
+//   phase A :  S(j+1) = K(j+1) Q^T          with P = exp of keys 0..31 of tile j
+//   phase B1:  O^T += V^T P^T, keys 0..31   with P = exp of keys 32..63 of tile j
+//   phase B2:  O^T += V^T P^T, keys 32..63
 //
-// so each phase pairs a run of MFMAs with independent vector work. The score
-// product of the next tile needs its K one tile earlier than its V, so K is
-// loaded two tiles ahead and V one tile ahead; both stay double-buffered and
-// one barrier per tile both publishes the loads and frees the buffers:
+// so each phase pairs a run of MFMAs with independent vector work. Every
+// tile's K and V are loaded one step ahead (K of tile j+2 and V of tile j+1
+// during step j), double-buffered; one barrier per half-step publishes the
+// loads issued in the half-step before it and frees the buffers read there.
 //
-//   after the barrier of tile j:  load K(j+2) -> the K buffer of tile j,
-//                                 load V(j+1) -> the V buffer of tile j-1.
-//
-// The softmax state follows the same lazy rescale as the other kernels: the
-// running reference m only moves (and O and the sums are only rescaled) when
-// a tile's row maximum exceeds it by more than 2^kRescaleSlack. The rescale
-// of O waits for the P.V product that precedes it in phase B.
+// P is formed against a lazy reference m: while a lane's sum of its 16 P of a
+// half tile stays within 2^kRescaleSlack (so every P is within the bound) the
+// P are kept; otherwise the half tile's exact maximum decides, and when it
+// exceeds m by more than the slack, m moves, O and the sums are rescaled and
+// that half's P is formed again (the sum guard, commit_half).
 // ---------------------------------------------------------------------------
 //
 // SPLIT: split-KV partials. Item = (head, split, query tile); split s visits
@@ -644,7 +632,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       l_run += lt;
       l_rnd += ltr;
     };
-#if RF_ATT_SPLITEXP
     static_assert(MB == 2, "two halves per tile");
     // Steady-state step with the exponentials split across both phases:
     //   phase A : S(next) MFMAs     with the exponentials of keys 0..31
@@ -729,109 +716,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         pv_range(vs_cur, pk, NPV / 2, NPV, [](int) {});
       }
     };
-#else
-    // One steady-state step: current tile (scores s_cur, V in vs_cur), next tile
-    // (K in ks_next, scores into s_next).
-    auto step = [&](const uint16_t* ks_next, const uint16_t* vs_cur, f32x16_t (&s_cur)[MB],
-                    f32x16_t (&s_next)[MB], int kt_next, bool mine_next, int part_next,
-                    const uint64_t* bb_next) {
-      uint32_t pk[MB][8];
-      // d = 64 has registers to spare: read the word before phase A.
-      const uint64_t word_next = D <= 64 ? row_word(part_next, bb_next) : 0;
-      float lt = 0.f, ltr = 0.f;
-      // Phase A: score product of the next tile with the exponentials of this
-      // one, written as NS chunks of one MFMA plus its share of the vector work
-      // (fenced so the compiler keeps the interleave).
-      {
-#pragma unroll
-        for (int a = 0; a < MB; ++a)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s_next[a][r] = 0.f;
-        constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
-        constexpr int PAIRS = MB * 8;             // score pairs per lane and tile
-        constexpr int PPC = (PAIRS + NS - 1) / NS;  // pairs per chunk
-        auto kread = [&](int i) {
-          const int kstep = i / MB, mb = i % MB;
-          const int row = 32 * mb + l32;
-          return *reinterpret_cast<const uint4*>(ks_next + row * D + 8 * SW::k_slot(row, 2 * kstep + h));
-        };
-        const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
-        uint4 kfrag[KAHEAD];
-#pragma unroll
-        for (int i = 0; i < KAHEAD; ++i) kfrag[i] = kread(i);
-#pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const int kstep = i / MB, mb = i % MB;
-          const uint4 a = kfrag[i % KAHEAD];
-          if (i + KAHEAD < NS) kfrag[i % KAHEAD] = kread(i + KAHEAD);
-          s_next[mb] = mfma32(as_bf16x8(a), as_bf16x8(qf[kstep]), s_next[mb]);
-#pragma unroll
-          for (int j = 0; j < PPC; ++j) {
-            const int pr = i * PPC + j;
-            if (pr < PAIRS) {
-              const int cb = pr / 8, r = 2 * (pr % 8);
-              const float p0 = fast_exp2(fmaf(s_cur[cb][r], c_exp, -mu));
-              const float p1 = fast_exp2(fmaf(s_cur[cb][r + 1], c_exp, -mu));
-              const uint32_t pp = cvt_pk_bf16(p0, p1);
-              lt += p0 + p1;
-              ltr = add_bf16_pair(pp, ltr);
-              pk[cb][r >> 1] = pp;
-            }
-          }
-#if RF_ATT_SP_SCHED
-          __builtin_amdgcn_sched_barrier(0);
-#endif
-        }
-      }
-      // Keep P and the sums in phase A: without these uses the compiler sinks
-      // the exponentials past the mask branch, next to the P.V product.
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[mb][i]));
-      asm volatile("" ::"v"(lt), "v"(ltr));
-#if RF_ATT_SUMGUARD
-      commit_tile(s_cur, pk, lt, ltr);
-      mod_tile(s_next, kt_next);
-      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
-      // Phase B: P.V product of this tile.
-      pv_mfmas(vs_cur, pk);
-#else
-      l_run += lt;
-      l_rnd += ltr;
-      mod_tile(s_next, kt_next);
-      mask_tile(s_next, kt_next, mine_next, part_next, D <= 64 ? word_next : row_word(part_next, bb_next));
-      // Phase B: P.V product of this tile with the row maximum of the next one.
-      pv_mfmas(vs_cur, pk);
-      bool moved = false;
-      const float alpha = tile_max(s_next, &moved);
-#if RF_ATT_SP_SCHED
-      {
-        constexpr int VAHEAD = RF_ATT_VREAD_AHEAD > 0 ? RF_ATT_VREAD_AHEAD : 1;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * VAHEAD, 1);
-#pragma unroll
-        for (int i = 0; i < NPV; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-          if (i < NPV - VAHEAD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-          __builtin_amdgcn_sched_group_barrier(0x002, RF_ATT_SP_VALU_B, 1);
-        }
-      }
-#endif
-      if (moved) rescale(alpha);
-#endif
-    };
-#endif
     // The last tile: exponentials and P.V product only.
     auto finish = [&](const uint16_t* vs_cur, const f32x16_t (&s_cur)[MB]) {
       uint32_t pk[MB][8];
       float lt = 0.f, ltr = 0.f;
       exp_tile(s_cur, pk, lt, ltr);
-#if RF_ATT_SUMGUARD
       commit_tile(s_cur, pk, lt, ltr);
-#else
-      l_run += lt;
-      l_rnd += ltr;
-#endif
       pv_mfmas(vs_cur, pk);
     };
     f32x16_t s0[MB], s1[MB];

@@ -1,18 +1,21 @@
-"""Per-launch HBM traffic of each kernel from two rocprofv3 counter runs.
+"""Per-launch HBM traffic of each kernel from rocprofv3 counter runs.
 
-    python -m online_softmax_attention_pass_amd.traffic FETCH_CSV WRITE_CSV OUT_JSON
+    python -m online_softmax_attention_pass_amd.traffic OUT_JSON RUN [RUN ...]
+    RUN = WORKLOADS:FETCH_CSV:WRITE_CSV
 
-FETCH_CSV / WRITE_CSV are the ``*_counter_collection.csv`` files of two
-``rocprofv3 --pmc FETCH_SIZE`` and ``rocprofv3 --pmc WRITE_SIZE`` runs of
-``bench.py --workloads copy,...``. Both counters are read per dispatch in KiB
-and averaged over the dispatches of each kernel. They are then scaled by the
-ratio the same counter shows for the calibration copy (a torch elementwise
-kernel over 1 GiB fp32: 2^30 bytes read and 2^30 bytes written per dispatch),
-so the figures are HBM bytes in the units the copy defines.
+Each RUN is one ``bench.py --workloads WORKLOADS`` invocation profiled twice,
+with ``rocprofv3 --pmc FETCH_SIZE`` and with ``--pmc WRITE_SIZE``; FETCH_CSV and
+WRITE_CSV are the two ``*_counter_collection.csv`` files. Both counters are
+read per dispatch in KiB and averaged over the dispatches of each kernel, then
+scaled by the ratio the same counter shows for the calibration copy (a torch
+elementwise kernel over 1 GiB fp32: 2^30 bytes read and 2^30 bytes written per
+dispatch), which the first run must include (workload ``copy``). Workloads
+that share a kernel instance go in different runs: within a run, a kernel is
+attributed to the one listed workload that uses it.
 
 The output maps each workload to its kernel's bytes per launch together with
-the sha256 of the kernel source (and the headers it includes) it was measured on; bench.py reports the
-figure only while that source is unchanged.
+the sha256 of the kernel source (and the headers it includes) it was measured
+on; bench.py reports the figure only while that source is unchanged.
 """
 from __future__ import annotations
 
@@ -26,16 +29,21 @@ from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
-# (substring of the kernel name, workload, kernel source)
-KERNELS = [
-    ("softmax_rows", "softmax", "softmax_rows.hip"),
-    ("layernorm_rows", "layernorm", "layernorm_rows.hip"),
-    ("attention_bf16_sp_kernel<128, 4, 2, false>", "prefill", "attention_bf16.hip"),
-    ("attention_bf16_sp_kernel<64, 2, 2, false>", "sparse", "attention_bf16.hip"),
-    ("attention_bf16_sp_kernel<64, 2, 2, true>", "bitmap", "attention_bf16.hip"),
-    ("decode_partial_kernel", "decode", "decode_splitkv.hip"),
-    ("attention_f32", "attn_f32", "attention_f32.hip"),
-]
+# workload -> (substring of its dominant kernel's name, kernel source)
+KERNELS = {
+    "softmax": ("softmax_rows", "softmax_rows.hip"),
+    "layernorm": ("layernorm_rows", "layernorm_rows.hip"),
+    "prefill": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 0>", "attention_bf16.hip"),
+    "sparse": ("attention_bf16_sp_kernel<64, 2, 2, false, false, 0>", "attention_bf16.hip"),
+    "bitmap": ("attention_bf16_sp_kernel<64, 2, 2, true, false, 0>", "attention_bf16.hip"),
+    "decode": ("decode_partial_kernel", "decode_splitkv.hip"),
+    "attn_f32": ("attention_f32", "attention_f32.hip"),
+    "gqa": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0>", "attention_bf16.hip"),
+    "mla": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0>", "attention_bf16.hip"),
+    "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
+    "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
+    "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2>", "attention_bf16.hip"),
+}
 COPY_KEY = "MulFunctor"
 COPY_BYTES = float(1 << 30)
 
@@ -80,20 +88,35 @@ def find(table: dict, key: str):
 
 
 def main(argv):
-    if len(argv) != 3:
+    if len(argv) < 2:
         raise SystemExit(__doc__)
-    fetch = per_kernel_kib(argv[0], "FETCH_SIZE")
-    write = per_kernel_kib(argv[1], "WRITE_SIZE")
-    f_scale = COPY_BYTES / find(fetch, COPY_KEY)
-    w_scale = COPY_BYTES / find(write, COPY_KEY)
+    out_path, runs = argv[0], []
+    for spec in argv[1:]:
+        wl, fcsv, wcsv = spec.split(":")
+        runs.append(([w for w in wl.split(",") if w], per_kernel_kib(fcsv, "FETCH_SIZE"),
+                     per_kernel_kib(wcsv, "WRITE_SIZE")))
+    names0, fetch0, write0 = runs[0]
+    if "copy" not in names0:
+        raise SystemExit("the first run must include the copy calibration")
+    f_scale = COPY_BYTES / find(fetch0, COPY_KEY)
+    w_scale = COPY_BYTES / find(write0, COPY_KEY)
     out = {"calibration": {"copy_bytes_each_way": COPY_BYTES, "fetch_bytes_per_kib": f_scale,
                            "write_bytes_per_kib": w_scale}}
-    for key, workload, src in KERNELS:
-        fb = find(fetch, key) * f_scale
-        wb = find(write, key) * w_scale
-        out[workload] = {"kernel": key, "source_sha": source_sha(src), "fetch_bytes": round(fb),
-                         "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
-    with open(argv[2], "w") as f:
+    for names, fetch, write in runs:
+        for workload in names:
+            if workload == "copy":
+                continue
+            if workload not in KERNELS:
+                raise SystemExit(f"unknown workload {workload!r}")
+            shared = [w for w in names if w != workload and KERNELS.get(w, ("",))[0] == KERNELS[workload][0]]
+            if shared:
+                raise SystemExit(f"{workload} shares its kernel with {shared} in one run")
+            key, src = KERNELS[workload]
+            fb = find(fetch, key) * f_scale
+            wb = find(write, key) * w_scale
+            out[workload] = {"kernel": key, "source_sha": source_sha(src), "fetch_bytes": round(fb),
+                             "write_bytes": round(wb), "bytes_per_launch": round(fb + wb)}
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))

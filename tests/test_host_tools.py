@@ -29,14 +29,17 @@ def _write_counters(path, counter, rows):
             w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
 
 
+SP = "void rf::attention_bf16_sp_kernel<{}>(unsigned short const*)"
+
+
 def test_traffic_scales_by_the_copy_calibration(tmp_path):
     copy = "void at::native::vectorized_elementwise_kernel<4, AUnaryFunctor<MulFunctor<float> > >(int)"
     names = {
         "softmax": "void rf::softmax_rows_reg<float, 4, 512, 16>(float const*)",
         "layernorm": "void rf::layernorm_rows_reg<float, 4, 512, 16>(float const*)",
-        "prefill": "void rf::attention_bf16_sp_kernel<128, 4, 2, false>(unsigned short const*)",
-        "sparse": "void rf::attention_bf16_sp_kernel<64, 2, 2, false>(unsigned short const*)",
-        "bitmap": "void rf::attention_bf16_sp_kernel<64, 2, 2, true>(unsigned short const*)",
+        "prefill": SP.format("128, 4, 2, false, false, 0"),
+        "sparse": SP.format("64, 2, 2, false, false, 0"),
+        "bitmap": SP.format("64, 2, 2, true, false, 0"),
         "decode": "void rf::decode_partial_kernel<128, 8>(unsigned short const*)",
         "attn_f32": "void rf::attention_f32_kernel<64>(float const*)",
     }
@@ -47,7 +50,7 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     fcsv, wcsv, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "t.json"
     _write_counters(fcsv, "FETCH_SIZE", fetch)
     _write_counters(wcsv, "WRITE_SIZE", write)
-    traffic.main([str(fcsv), str(wcsv), str(out)])
+    traffic.main([str(out), f"copy,{','.join(names)}:{fcsv}:{wcsv}"])
     t = json.load(open(out))
     assert t["calibration"]["fetch_bytes_per_kib"] == pytest.approx(2048.0)
     assert t["calibration"]["write_bytes_per_kib"] == pytest.approx(1024.0)
@@ -60,6 +63,28 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     assert t["prefill"]["source_sha"] == traffic.source_sha("attention_bf16.hip")
 
 
+def test_traffic_keeps_shared_kernels_apart_by_run(tmp_path):
+    """Grouped-query and shared-cache decode use one kernel instance, as do the
+    ALiBi and window legs: each pair is measured in different runs."""
+    copy = "vectorized_elementwise_kernel<MulFunctor>"
+    split, mod1 = SP.format("128, 4, 2, false, true, 0"), SP.format("128, 4, 2, false, false, 1")
+    runs = []
+    for r, (wl, kf) in enumerate((("copy,gqa,alibi", 100.0), ("mla,window", 300.0))):
+        rows = ([(copy, 524288.0)] if r == 0 else []) + [(split, kf), (mod1, kf + 1)]
+        wrows = ([(copy, 1048576.0)] if r == 0 else []) + [(split, kf), (mod1, kf + 1)]
+        f, w = tmp_path / f"f{r}.csv", tmp_path / f"w{r}.csv"
+        _write_counters(f, "FETCH_SIZE", rows)
+        _write_counters(w, "WRITE_SIZE", wrows)
+        runs.append(f"{wl}:{f}:{w}")
+    out = tmp_path / "t.json"
+    traffic.main([str(out)] + runs)
+    t = json.load(open(out))
+    assert t["gqa"]["fetch_bytes"] == 100 * 2048 and t["alibi"]["fetch_bytes"] == 101 * 2048
+    assert t["mla"]["fetch_bytes"] == 300 * 2048 and t["window"]["write_bytes"] == 301 * 1024
+    with pytest.raises(SystemExit):                    # one run may not hold both users of a kernel
+        traffic.main([str(out), runs[0].replace("copy,gqa,alibi", "copy,gqa,mla")])
+
+
 def test_traffic_rejects_an_ambiguous_kernel(tmp_path):
     copy = "vectorized_elementwise_kernel<MulFunctor>"
     rows = [(copy, 1.0), ("softmax_rows_reg<float, 4>", 1.0), ("softmax_rows_stream<float>", 1.0)]
@@ -67,7 +92,7 @@ def test_traffic_rejects_an_ambiguous_kernel(tmp_path):
     _write_counters(fcsv, "FETCH_SIZE", rows)
     _write_counters(wcsv, "WRITE_SIZE", rows)
     with pytest.raises(SystemExit):
-        traffic.main([str(fcsv), str(wcsv), str(tmp_path / "t.json")])
+        traffic.main([str(tmp_path / "t.json"), f"copy,softmax:{fcsv}:{wcsv}"])
 
 
 def test_bench_reports_traffic_only_for_the_measured_source(tmp_path, monkeypatch):
