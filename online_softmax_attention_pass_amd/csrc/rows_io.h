@@ -1,4 +1,5 @@
-// Row element access shared by the row kernels (softmax, layer norm): fp32 or
+// Row element access (and one lane exchange) shared by the row kernels
+// (softmax, layer norm): fp32 or
 // bf16 (raw bits), as 16-byte vectors of EPV elements, or single elements
 // (EPV = 1) when a row is not 16-byte aligned. Loads and stores are
 // non-temporal: every element is touched once.
@@ -49,6 +50,11 @@ template <> struct Io<uint16_t, 1> {
   __device__ static void load(const uint16_t* p, float (&o)[1]) { o[0] = bf16_to_f32(*p); }
   __device__ static void store(uint16_t* p, const float (&o)[1]) { *p = uint16_t(f32_to_bf16_bits(o[0])); }
 };
+
+// Lane l exchanges x with lane l ^ 16 (ds_swizzle, bit mode: and 0x1f, xor 16).
+__device__ __forceinline__ float swizzle_xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F));
+}
 
 typedef uint32_t buf_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufNonTemporal = 2;  // cache policy bit: non-temporal

@@ -19,19 +19,46 @@
 namespace rf {
 namespace {
 
-// Workgroup-wide (+)-reduction of (m, l): wavefront butterfly, then LDS across waves.
+// One butterfly level of the (m, l) tree: this lane's pair meets (m2, l2), the
+// pair of the lane group it is paired with. The lower group's pair always goes
+// first, so both sides evaluate the same expression and hold identical bits.
+__device__ __forceinline__ void ml_level(float& m, float& l, float m2, float l2, bool upper) {
+  float am = upper ? m2 : m, al = upper ? l2 : l;
+  const float bm = upper ? m : m2, bl = upper ? l : l2;
+  ml_combine_nat(am, al, bm, bl);
+  m = am;
+  l = al;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void ml_dpp_level(float& m, float& l, bool upper) {
+  ml_level(m, l, dpp_mov<CTRL>(m), dpp_mov<CTRL>(l), upper);
+}
+
+// Workgroup-wide (+)-reduction of (m, l) with no lane-address registers: DPP
+// within rows of 16 lanes, a swizzle across the two rows of each half,
+// v_permlane32_swap across the halves, then LDS across waves. Every lane ends
+// with the same bits.
 template <int BLOCK>
 __device__ __forceinline__ void block_combine(float& m, float& l, float* sm, float* sl) {
   constexpr int NW = BLOCK / 64;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float m2 = shfl_xor(m, off);
-    const float l2 = shfl_xor(l, off);
-    ml_combine_nat(m, l, m2, l2);
-  }
+  const int lane = threadIdx.x & 63;
+  ml_dpp_level<0xB1>(m, l, lane & 1);
+  ml_dpp_level<0x4E>(m, l, lane & 2);
+  ml_dpp_level<0x141>(m, l, lane & 4);
+  ml_dpp_level<0x140>(m, l, lane & 8);
+  ml_level(m, l, swizzle_xor16(m), swizzle_xor16(l), lane & 16);
+  const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  const auto rl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+  m = __uint_as_float(rm[0]);  // low half first
+  l = __uint_as_float(rl[0]);
+  ml_combine_nat(m, l, __uint_as_float(rm[1]), __uint_as_float(rl[1]));
   if constexpr (NW > 1) {
     const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) { sm[w] = m; sl[w] = l; }
+    if (lane == 0) {
+      sm[w] = m;
+      sl[w] = l;
+    }
     __syncthreads();
     m = sm[0];
     l = sl[0];
@@ -40,32 +67,34 @@ __device__ __forceinline__ void block_combine(float& m, float& l, float* sm, flo
   }
 }
 
-// Register-resident row: thread t owns vectors t, t + BLOCK, ..., t + (NV-1) BLOCK.
+// Register-resident row: thread t owns vectors t, t + BLOCK, ..., t + (NV-1) BLOCK
+// of EPV elements. Every access goes through row-sized buffer resources: the
+// vectors past the row's end read 0 and are never written, with no branches;
+// the reduction replaces them by -inf.
 template <typename T, int EPV, int BLOCK, int NV>
-__global__ __launch_bounds__(BLOCK) void softmax_rows_reg(const T* __restrict__ x, T* __restrict__ y,
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(BLOCK == 1024 && EPV > 1 && NV * EPV == 32 ? 8 : 1))) void softmax_rows_reg(const T* __restrict__ x, T* __restrict__ y,
                                                           int64_t rows, int64_t cols) {
   __shared__ float sm[BLOCK / 64], sl[BLOCK / 64];
-  const int64_t nvec = cols / EPV;  // the host guarantees cols % EPV == 0
+  constexpr uint32_t VB = EPV * sizeof(T);  // bytes per vector
+  const int64_t nvec = cols / EPV;          // the host guarantees cols % EPV == 0
+  const uint32_t row_bytes = uint32_t(cols) * uint32_t(sizeof(T));
+  const int64_t owned = (nvec - int64_t(threadIdx.x) + BLOCK - 1) / BLOCK;
+  const int nv = int(owned < NV ? owned : NV);  // vectors of this lane inside the row
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
-    const T* xr = x + r * cols;
-    T* yr = y + r * cols;
+    const __amdgpu_buffer_rsrc_t xs = row_rsrc(x + r * cols, row_bytes);
+    const __amdgpu_buffer_rsrc_t ys = row_rsrc(y + r * cols, row_bytes);
     float v[NV][EPV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int64_t vi = threadIdx.x + int64_t(k) * BLOCK;
-      if (vi < nvec) {
-        Io<T, EPV>::load(xr + vi * EPV, v[k]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) v[k][e] = kNegInf;
-      }
-    }
+    for (int k = 0; k < NV; ++k) BufIo<T, EPV>::load(xs, (threadIdx.x + k * BLOCK) * VB, v[k]);
     // Lane-local pair: m_t = max of its elements, l_t = sum_e e^{x_e - m_t}.
     float m = kNegInf;
 #pragma unroll
     for (int k = 0; k < NV; ++k)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) m = fmaxf(m, v[k][e]);
+      for (int e = 0; e < EPV; ++e) {
+        v[k][e] = k < nv ? v[k][e] : kNegInf;
+        m = fmaxf(m, v[k][e]);
+      }
     const float mu = (m == kNegInf) ? 0.f : m;
     float l = 0.f;
 #pragma unroll
@@ -79,14 +108,15 @@ __global__ __launch_bounds__(BLOCK) void softmax_rows_reg(const T* __restrict__ 
     block_combine<BLOCK>(M, L, sm, sl);
     // y = e^{x - m_t} * e^{m_t - M} / L  (an all -inf row gives NaN, as the definition does)
     const float c = fast_exp2((m - M) * kLog2e) / L;
+    // Store offsets are recomputed from an opaque copy of the lane index, so
+    // the load offsets need not stay live across the reduction.
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-      const int64_t vi = threadIdx.x + int64_t(k) * BLOCK;
-      if (vi < nvec) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) v[k][e] *= c;
-        Io<T, EPV>::store(yr + vi * EPV, v[k]);
-      }
+      for (int e = 0; e < EPV; ++e) v[k][e] *= c;
+      BufIo<T, EPV>::store(ys, (t + k * BLOCK) * VB, v[k]);
     }
     if (BLOCK > 64 && r + gridDim.x < rows) __syncthreads();  // sm/sl reused by the next row
   }
@@ -129,9 +159,11 @@ __global__ __launch_bounds__(BLOCK) void softmax_rows_stream(const T* __restrict
   }
 }
 
-// Register-resident variants, smallest first: (lanes per workgroup, floats per lane).
-// At most 64 row elements live in each lane, so even the 1024-lane variant
-// (16 waves, 4 per SIMD) stays within 128 VGPRs without spilling.
+// Register-resident variants, smallest first: (lanes per workgroup, elements per
+// lane). Each stays within the VGPRs of its occupancy without spilling; a row of
+// 16k-32k elements goes to 1024 lanes x 32 (64 VGPRs: two workgroups, eight waves
+// per SIMD), which streams faster than 512 lanes x 64 (two workgroups, four waves
+// per SIMD).
 template <typename T, int EPV>
 hipError_t dispatch(const T* x, T* y, int64_t rows, int64_t cols, hipStream_t stream) {
   const int64_t nvec = cols / EPV;
@@ -146,6 +178,7 @@ hipError_t dispatch(const T* x, T* y, int64_t rows, int64_t cols, hipStream_t st
   RF_SOFTMAX_REG(128, 32)
   RF_SOFTMAX_REG(256, 32)
   RF_SOFTMAX_REG(512, 32)
+  RF_SOFTMAX_REG(1024, 32)
   RF_SOFTMAX_REG(512, 64)
   RF_SOFTMAX_REG(1024, 64)
 #undef RF_SOFTMAX_REG
