@@ -15,6 +15,7 @@ from .oracle import (  # noqa: F401
     element_mask,
     layernorm_rows,
     logsumexp_rows,
+    moe_route,
     lse_merge,
     online_attention,
     online_softmax_stats,

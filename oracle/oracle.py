@@ -267,6 +267,27 @@ def attention_score_mod(q, k, v, scale: float, causal: bool = False, block_mask=
     return O, LSE
 
 
+def moe_route(logits, k: int, renorm: bool):
+    """Mixture-of-experts routing, in fp64: the softmax over each token's expert
+    logits, then its k largest probabilities (RedFuser page, 1. Problématique:
+    MoE routing as a cascaded reduction; 4. Résultats Expérimentaux).
+
+    logits: [T, E]. The softmax is monotone, so the selected experts are the k
+    largest logits, taken largest first, equal logits by lower expert index (a
+    stable sort of the exact inputs: no rounding decides the choice). Weights:
+      p_e = exp(x_e - m) / sum_j exp(x_j - m)           (three passes)
+      w_r = p_{idx_r}, or p_{idx_r} / sum_{r'} p_{idx_r'} with renorm.
+    Returns (idx int32 [T, k], w float64 [T, k]).
+    """
+    x = np.asarray(logits, dtype=np.float64)
+    idx = np.argsort(-x, axis=-1, kind="stable")[:, :k].astype(np.int32)
+    p = softmax_rows(x)
+    w = np.take_along_axis(p, idx, axis=-1)
+    if renorm:
+        w = w / w.sum(axis=-1, keepdims=True)
+    return idx, w
+
+
 def decode_gqa(q, k, v, scale: float):
     """Decode with grouped queries, in fp64: one token per query head, and
     query heads that share key/value heads (RedFuser page, 4. Résultats

@@ -1052,3 +1052,103 @@ def test_score_mod_mutants_are_caught(kind):
         assert not (pin_mod_bruteforce(fn) and pin_mod_reductions(fn) and pin_mod_closed_forms(fn))
     none = _mod_mutant("none")
     assert pin_mod_bruteforce(none) and pin_mod_reductions(none) and pin_mod_closed_forms(none)
+
+
+# ---------------------------------------------------------------------------
+# mixture-of-experts routing: softmax over experts, then the top k
+# ---------------------------------------------------------------------------
+
+def pin_moe_bruteforce(fn):
+    """Pure Python: sort by (-x, index), math.exp / math.fsum probabilities."""
+    r = np.random.default_rng(61)
+    x = r.normal(0, 2, size=(7, 13))
+    x[3, 5] = x[3, 9] = x[3].max() + 1.0            # a tie at the top
+    for k in (1, 4, 13):
+        for renorm in (False, True):
+            idx, w = fn(x, k, renorm)
+            for t in range(7):
+                row = [float(v) for v in x[t]]
+                order = sorted(range(13), key=lambda e: (-row[e], e))[:k]
+                m = max(row)
+                z = math.fsum(math.exp(v - m) for v in row)
+                p = [math.exp(row[e] - m) / z for e in order]
+                if renorm:
+                    s = math.fsum(p)
+                    p = [v / s for v in p]
+                if list(idx[t]) != order or max(abs(w[t, i] - p[i]) for i in range(k)) > 1e-15:
+                    return False
+    return True
+
+
+def pin_moe_closed_forms(fn):
+    # logits ln 1, ln 2, ln 3, ln 2: probabilities 1/8, 2/8, 3/8, 2/8
+    x = np.log(np.array([[1.0, 2.0, 3.0, 2.0]]))
+    idx, w = fn(x, 3, False)
+    if idx.tolist() != [[2, 1, 3]] or np.max(np.abs(w - [[3 / 8, 2 / 8, 2 / 8]])) > 1e-15:
+        return False
+    idx, w = fn(x, 2, True)                            # renormalised over the two kept
+    if idx.tolist() != [[2, 1]] or np.max(np.abs(w - [[0.6, 0.4]])) > 1e-15:
+        return False
+    # equal logits: the lowest indices, each 1/E (or 1/k renormalised); k = 1 renormalised weighs exactly 1
+    x = np.full((2, 6), 0.25)
+    idx, w = fn(x, 3, False)
+    if idx.tolist() != [[0, 1, 2]] * 2 or np.max(np.abs(w - 1 / 6)) > 1e-15:
+        return False
+    idx, w = fn(x, 3, True)
+    if np.max(np.abs(w - 1 / 3)) > 1e-15:
+        return False
+    idx, w = fn(np.random.default_rng(62).normal(size=(5, 9)), 1, True)
+    return bool(np.all(w == 1.0))
+
+
+def pin_moe_invariances(fn):
+    r = np.random.default_rng(63)
+    x = r.normal(0, 3, size=(6, 40))
+    for k, renorm in ((8, False), (8, True), (40, False)):
+        idx0, w0 = fn(x, k, renorm)
+        if k == 40 and not renorm and abs(float(w0.sum(axis=1).max()) - 1) > 1e-14:   # every expert: sums to 1
+            return False
+        for c in (1000.0, -1000.0):                   # shift invariance (the naive form overflows at +1000)
+            idx, w = fn(x + c, k, renorm)
+            if not np.array_equal(idx, idx0) or not np.all(np.abs(w - w0) <= 1e-12):   # NaN fails too
+                return False
+    return True
+
+
+def test_moe_route_pins():
+    assert pin_moe_bruteforce(O.moe_route)
+    assert pin_moe_closed_forms(O.moe_route)
+    assert pin_moe_invariances(O.moe_route)
+
+
+def _moe_mutant(kind):
+    def fn(logits, k, renorm):
+        x = np.asarray(logits, np.float64)
+        if kind == "ascending":
+            idx = np.argsort(x, axis=-1, kind="stable")[:, :k]
+        elif kind == "ties_high_index":
+            idx = (x.shape[1] - 1 - np.argsort(-x[:, ::-1], axis=-1, kind="stable"))[:, :k]
+        else:
+            idx = np.argsort(-x, axis=-1, kind="stable")[:, :k]
+        if kind == "no_shift":
+            with np.errstate(all="ignore"):
+                e = np.exp(x)
+                p = e / e.sum(axis=-1, keepdims=True)
+        else:
+            p = O.softmax_rows(x)
+        w = np.take_along_axis(p, idx, axis=-1)
+        if renorm and kind != "renorm_ignored":
+            w = w / w.sum(axis=-1, keepdims=True)
+        if kind == "always_renorm" and not renorm:
+            w = w / w.sum(axis=-1, keepdims=True)
+        return idx.astype(np.int32), w
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["ascending", "ties_high_index", "no_shift", "renorm_ignored", "always_renorm"])
+def test_moe_route_mutants_are_caught(kind):
+    fn = _moe_mutant(kind)
+    with np.errstate(all="ignore"):
+        assert not (pin_moe_bruteforce(fn) and pin_moe_closed_forms(fn) and pin_moe_invariances(fn))
+    none = _moe_mutant("none")
+    assert pin_moe_bruteforce(none) and pin_moe_closed_forms(none) and pin_moe_invariances(none)

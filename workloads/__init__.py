@@ -220,7 +220,25 @@ EXTENSION_CONFIGS = {
     "score_mod": dict(name="score_mod_bf16_B4_H32_L4096_d128", kind="attention", dtype="bf16", B=4, H=32,
                       Lq=4096, Lk=4096, d=128, scale=1.0 / math.sqrt(128), causal=True, softcap=50.0,
                       window=1024, seed=10),
+    # Mixture-of-experts routing: router logits of 131072 tokens over 256
+    # experts, top 8 renormalised (a large-expert-count layer).
+    "moe": dict(name="moe_route_f32_T131072_E256_k8", kind="moe", dtype="f32", T=131072, E=256, k=8, renorm=True,
+                seed=11),
 }
+
+TID_LOGITS = 8
+
+
+def moe_logits(seed: int, T: int, E: int, quantum: float = 0.0) -> np.ndarray:
+    """Router logits [T, E] float32 ~ N(0, 2^2), drawn per token; quantum > 0
+    rounds them to multiples of it (many exact ties)."""
+    x = np.empty((T, E), np.float32)
+    for t0 in range(0, T, 4096):
+        t1 = min(T, t0 + 4096)
+        x[t0:t1] = 2.0 * rng(seed, TID_LOGITS, t0).standard_normal((t1 - t0, E), dtype=np.float32)
+    if quantum > 0:
+        x = (np.round(x / quantum) * quantum).astype(np.float32)
+    return x
 
 
 def alibi_slopes(H: int) -> np.ndarray:
