@@ -16,7 +16,8 @@ grouped queries at Lk 32768, d 128: 8 query heads per key/value head (B64 Hq64
 Hkv8, 4 splits) and 128 query heads on one cache (B64 Hq128 Hkv1, 16 splits),
 in GB/s with TFLOP/s alongside; and the score modifications on the causal
 prefill shape (B4 H32 L4096 d128): ALiBi bias, tanh softcap 50, and a
-1024-key sliding window (TFLOP/s).
+1024-key sliding window (TFLOP/s); and mixture-of-experts routing of 131072
+tokens over 256 experts, top 8 (GB/s).
 
 Timing: inputs are resident in HBM before the timed region; W untimed
 warm-up calls; then K calls, each bracketed by HIP events recorded on the
@@ -50,6 +51,7 @@ KERNEL_SOURCES = {
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip", "bitmap": "attention_bf16.hip",
     "layernorm": "layernorm_rows.hip", "gqa": "attention_bf16.hip", "mla": "attention_bf16.hip",
     "alibi": "attention_bf16.hip", "softcap": "attention_bf16.hip", "window": "attention_bf16.hip",
+    "moe": "moe_route.hip",
 }
 
 
@@ -296,6 +298,22 @@ def setup_mla_decode(rf, torch, W):
     return _setup_gqa(rf, torch, W, "mla_decode")
 
 
+def setup_moe(rf, torch, W):
+    c = W.EXTENSION_CONFIGS["moe"]
+    T, E, k = c["T"], c["E"], c["k"]
+    # two sets of logits (128 MiB each), alternated so no call is served from the Infinity Cache
+    sets = [torch.from_numpy(W.moe_logits(c["seed"] + i, T, E)).cuda() for i in range(2)]
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    state = {"i": 0}
+
+    def fn():
+        x = sets[state["i"] % 2]
+        state["i"] += 1
+        rf.rf_moe_route(x, k, c["renorm"], out_idx=idx, out_w=w)
+    return dict(fn=fn, work=T * E * 4 + T * k * 8, unit="GB/s", bound="hbm", keep=(sets, idx, w), cfg=c)
+
+
 def setup_attn_f32(rf, torch, W):
     c = W.CONFIGS[1]
     q, k, v = (torch.from_numpy(W.normal_tensor(1, t, 1, 1, 128, 64, "f32")).cuda()
@@ -318,7 +336,7 @@ def setup_copy(rf, torch, W):
 
 
 SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse, "gqa": setup_gqa_decode, "mla": setup_mla_decode,
-          "alibi": setup_alibi, "softcap": setup_softcap, "window": setup_window,
+          "alibi": setup_alibi, "softcap": setup_softcap, "window": setup_window, "moe": setup_moe,
           "attn_f32": setup_attn_f32}
 
 
@@ -357,7 +375,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
-                    default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window")
+                    default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

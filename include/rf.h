@@ -78,6 +78,29 @@ typedef enum {
 int rf_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int dtype, void* stream);
 
 /*
+ * Mixture-of-experts routing: for each token t, the softmax over its E expert
+ * logits and its k most probable experts.
+ *   p_te = exp(x_te - m_t) / sum_j exp(x_tj - m_t),  m_t = max_j x_tj;
+ *   topk_idx[t, r] = the r-th expert in descending order of x_t (equal logits:
+ *                    lower expert index first; the softmax is monotone, so this
+ *                    is the order of p_t);
+ *   topk_w[t, r]   = p_t,idx, or p_t,idx / sum_r' p_t,idx[r'] when renorm != 0.
+ * Source: RedFuser page, 1. Problématique (MoE routing among the cascaded
+ * reductions: max, sum of exponentials, normalisation, then the selection) and
+ * 4. Résultats Expérimentaux (MoE routing workload).
+ *   logits   : [T, E] of `dtype` (RF_F32 or RF_BF16), device pointer.
+ *   topk_idx : int32 [T, k], written;  topk_w : fp32 [T, k], written.
+ *   1 <= k <= E. Each logit is read once.
+ * A token whose logits are all -inf gets NaN weights, as the definition does.
+ * Supported: E <= 1024, k <= 32 (else RF_ERR_UNSUPPORTED).
+ * Errors: RF_ERR_INVALID_ARG (unknown dtype, T < 0, E < 1, k outside 1..E,
+ * overflow, NULL or misaligned pointers with T > 0), RF_ERR_UNSUPPORTED,
+ * RF_ERR_HIP.
+ */
+int rf_moe_route(const void* logits, int32_t* topk_idx, float* topk_w, int64_t T, int E, int k, int renorm,
+                 int dtype, void* stream);
+
+/*
  * Row-wise layer normalisation: per row r, with n = cols,
  *   mean_r = (1/n) sum_j x_rj,  var_r = (1/n) sum_j (x_rj - mean_r)^2,
  *   y_rj   = (x_rj - mean_r) / sqrt(var_r + eps) * gamma_j + beta_j.
@@ -279,7 +302,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 4
+#define RF_ABI_VERSION 5
 int rf_abi_version(void);
 
 #ifdef __cplusplus

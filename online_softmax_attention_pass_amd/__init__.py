@@ -19,7 +19,7 @@ __all__ = [
     "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_fwd_mod",
     "rf_attention_decode_splitkv",
     "rf_attention_decode_splitkv_workspace_size", "rf_attention_decode_gqa", "rf_attention_decode_gqa_workspace_size",
-    "rf_lse_merge", "rf_abi_version",
+    "rf_lse_merge", "rf_moe_route", "rf_abi_version",
 ]
 
 RF_F32, RF_BF16 = 0, 1
@@ -62,6 +62,7 @@ def load():
         "rf_attention_decode_gqa_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_gqa": ([P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
+        "rf_moe_route": ([P, P, P, I64, I, I, I, I, P], I),
         "rf_status_string": ([I], ctypes.c_char_p),
         "rf_last_error_message": ([], ctypes.c_char_p),
         "rf_abi_version": ([], I),
@@ -361,3 +362,22 @@ def rf_lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse=None, want_ls
                           _stream(dev))
     _check(st, "rf_lse_merge")
     return o, lse
+
+
+def rf_moe_route(logits, k, renorm=True, out_idx=None, out_w=None):
+    """Mixture-of-experts routing of logits [T, E] (fp32 or bf16): the k most probable experts of each
+    token under the softmax. Returns (idx int32 [T, k], w fp32 [T, k])."""
+    torch = _torch()
+    lib = load()
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    idx = torch.empty((T, k), dtype=torch.int32, device=logits.device) if out_idx is None else out_idx
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device) if out_w is None else out_w
+    if idx.shape != (T, k) or idx.dtype != torch.int32 or w.shape != (T, k) or w.dtype != torch.float32:
+        raise ValueError("out_idx must be int32 [T, k] and out_w fp32 [T, k]")
+    dev = _dev(logits, idx, w)
+    st = lib.rf_moe_route(_ptr(logits), _ptr(idx), _ptr(w), T, E, int(k), 1 if renorm else 0, _dtype_code(logits),
+                          _stream(dev))
+    _check(st, "rf_moe_route")
+    return idx, w

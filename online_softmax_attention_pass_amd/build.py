@@ -28,6 +28,7 @@ SOURCES = [
     "decode_splitkv.hip",
     "attention_f32.hip",
     "attention_bf16.hip",
+    "moe_route.hip",
 ]
 
 COMMON = [

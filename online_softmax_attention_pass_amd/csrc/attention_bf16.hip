@@ -40,6 +40,7 @@
 //     rows of one query tile).
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 
 namespace rf {

@@ -18,6 +18,7 @@
 // by the bf16 path.
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 
 namespace rf {

@@ -22,6 +22,7 @@
 // Scores are kept in log2 units: t = (q . k) * scale * log2(e), p = 2^(t - m).
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 
 namespace rf {

@@ -17,6 +17,7 @@
 // statistics read, then a normalising read and write).
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 #include "rows_io.h"
 

@@ -15,6 +15,7 @@
 // that matters is the S x d partial rows, read once.
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 
 namespace rf {

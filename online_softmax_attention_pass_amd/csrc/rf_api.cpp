@@ -13,6 +13,7 @@
 #include <string>
 
 #include "rf.h"
+#include "launch.h"
 #include "rf_internal.h"
 
 namespace {
@@ -134,6 +135,33 @@ int rf_layernorm_rows(const void* x, const float* gamma, const float* beta, void
     return fail(RF_ERR_HIP, "rf_layernorm_rows: %s", e.what());
   } catch (...) {
     return fail(RF_ERR_HIP, "rf_layernorm_rows: unknown exception");
+  }
+}
+
+int rf_moe_route(const void* logits, int32_t* topk_idx, float* topk_w, int64_t T, int E, int k, int renorm,
+                 int dtype, void* stream) {
+  const char* name = "rf_moe_route";
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+    if (T < 0) return fail(RF_ERR_INVALID_ARG, "%s: T < 0", name);
+    if (E < 1) return fail(RF_ERR_INVALID_ARG, "%s: E = %d < 1", name, E);
+    if (k < 1 || k > E) return fail(RF_ERR_INVALID_ARG, "%s: k = %d outside 1..E (E = %d)", name, k, E);
+    if (E > 1024 || k > 32) return fail(RF_ERR_UNSUPPORTED, "%s: needs E <= 1024 and k <= 32 (E = %d, k = %d)", name, E, k);
+    int64_t n = T, nk = T;
+    if (!mul_ok(n, E) || !mul_ok(n, 4) || !mul_ok(nk, k) || !mul_ok(nk, 4))
+      return fail(RF_ERR_INVALID_ARG, "%s: size overflows int64", name);
+    if (T == 0) return ok();
+    if (logits == nullptr || topk_idx == nullptr || topk_w == nullptr)
+      return fail(RF_ERR_INVALID_ARG, "%s: NULL logits, topk_idx or topk_w", name);
+    if (!aligned(logits, dtype == RF_F32 ? 4 : 2) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+      return fail(RF_ERR_INVALID_ARG, "%s: misaligned pointer", name);
+    return hip_status(rf::launch_moe_route(logits, topk_idx, topk_w, T, E, k, renorm != 0 ? 1 : 0, dtype,
+                                           static_cast<hipStream_t>(stream)),
+                      name);
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
   }
 }
 

@@ -13,6 +13,7 @@
 // one online (m, l) read, then a normalising read + write.
 #include <stdint.h>
 
+#include "launch.h"
 #include "rf_internal.h"
 #include "rows_io.h"
 

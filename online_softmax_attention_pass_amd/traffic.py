@@ -43,16 +43,22 @@ KERNELS = {
     "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
     "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
     "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2>", "attention_bf16.hip"),
+    "moe": ("moe_route_kernel", "moe_route.hip"),
 }
 COPY_KEY = "MulFunctor"
 COPY_BYTES = float(1 << 30)
 
 
+# Launcher declarations only: they cannot change a kernel's code.
+HASH_SKIP = {"launch.h"}
+
+
 def source_sha(name: str, csrc: str = CSRC) -> str:
     """sha256[:16] over a kernel source and, in include order, every local
-    header it pulls in (``#include "..."``, followed recursively)."""
+    header it pulls in (``#include "..."``, followed recursively), except the
+    launcher declarations."""
     h = hashlib.sha256()
-    seen = set()
+    seen = set(HASH_SKIP)
 
     def add(fname):
         if fname in seen:

@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 4
+    assert lib.rf_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -284,3 +284,24 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b|oracle/", text), f
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, 100, 64, 8, 1, 7), INVALID),            # dtype
+    ((FAKE, FAKE, FAKE, -1, 64, 8, 1, F32), INVALID),
+    ((FAKE, FAKE, FAKE, 100, 0, 1, 1, F32), INVALID),
+    ((FAKE, FAKE, FAKE, 100, 64, 0, 1, F32), INVALID),
+    ((FAKE, FAKE, FAKE, 100, 4, 5, 1, F32), INVALID),           # k > E
+    ((FAKE, FAKE, FAKE, 100, 2048, 8, 1, F32), UNSUP),          # E > 1024
+    ((FAKE, FAKE, FAKE, 100, 256, 33, 1, F32), UNSUP),          # k > 32
+    ((NUL, FAKE, FAKE, 100, 64, 8, 1, F32), INVALID),
+    ((FAKE, NUL, FAKE, 100, 64, 8, 1, BF16), INVALID),
+    ((FAKE, FAKE, NUL, 100, 64, 8, 0, F32), INVALID),
+    ((P(0x10002), FAKE, FAKE, 100, 64, 8, 1, F32), INVALID),    # fp32 logits misaligned
+    ((FAKE, FAKE, FAKE, 1 << 62, 1024, 8, 1, F32), INVALID),    # overflow
+    ((NUL, NUL, NUL, 0, 64, 8, 1, F32), OK),
+])
+def test_moe_route_validation(lib, args, code):
+    assert lib.rf_moe_route(*args, NUL) == code
+    if code != OK:
+        assert "rf_moe_route" in _msg(lib)

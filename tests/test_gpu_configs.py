@@ -252,3 +252,20 @@ def test_extension_gqa_full_size(rf_gpu, name):
         refs.append(ref_o[0, 0])
     _report(f"extension {name} ({len(picks)} query heads)", worst_o, worst_l, np.concatenate(refs))
     assert worst_o <= 1e-2 and worst_l <= 1e-3
+
+
+def test_extension_moe_route_full_size(rf_gpu):
+    """Routing of 131072 tokens over 256 experts (top 8, renormalised): every
+    token's experts against the oracle, exactly, and every weight."""
+    import torch
+    c = W.EXTENSION_CONFIGS["moe"]
+    x = W.moe_logits(c["seed"], c["T"], c["E"])
+    note("extension moe full size")
+    xd = dev_f32(x)
+    idx, w = rf_gpu.rf_moe_route(xd, c["k"], c["renorm"])
+    _same_again((idx, w), rf_gpu.rf_moe_route(xd, c["k"], c["renorm"]), "moe")
+    ref_idx, ref_w = O.moe_route(x.astype(np.float64), c["k"], c["renorm"])
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    e = float(np.abs(w.cpu().numpy().astype(np.float64) - ref_w).max())
+    assert e <= 1e-5
+    _report("extension moe", e, 0.0)
