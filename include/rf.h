@@ -204,6 +204,52 @@ int rf_attention_fwd_mod(const void* q, const void* k, const void* v, void* o, f
                          int dtype, void* stream);
 
 /*
+ * Row-wise masked attention: exactly what rf_attention_fwd_bitmap computes
+ * (causal rule, tile kinds, row bitmaps inside partial tiles), by the row
+ * kernel of the dual-kernel strategy: one wavefront per query row walks only
+ * the key tiles its mask row keeps and, inside them, only the groups of keys
+ * with a visible one, with lane-level reductions and no synchronisation across
+ * wavefronts. Suited to highly sparse masks on short sequences; the tile
+ * kernel (rf_attention_fwd_bitmap) to the rest. rf_attention_plan chooses.
+ * Source: STOF page, Méthodologie 1 (dual-kernel strategy: row-wise kernel and
+ * block-wise kernel, chosen by an analytic model).
+ *   tile_kind : uint8 [ceil(Lq/64), ceil(Lk/64)] device pointer or NULL (every
+ *               tile full); tile_bits : uint64 [same tiles, 64] or NULL (every
+ *               nonzero kind is a full tile), 8-byte aligned.
+ *   q, k, v, o, lse and scale as rf_attention_fwd; q, k, v, o 16-byte aligned.
+ * Supported: RF_BF16 with d in {64, 128}.
+ * Errors: RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP.
+ */
+int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                             const uint8_t* tile_kind, const uint64_t* tile_bits, int dtype, void* stream);
+
+/*
+ * The analytic kernel choice for a masked call (host only, no GPU work): from
+ * HOST copies of the mask (tile_kind / tile_bits as for rf_attention_fwd_rowwise,
+ * NULL allowed), counts the work of each kernel exactly:
+ *   tile_work  : 64 x 64 tiles of matrix-core work per head, i.e. for every
+ *                workgroup of query rows (128 rows at d = 128, 64 at d = 64)
+ *                the key tiles any of its rows needs, times rows / 64;
+ *   row_groups : key groups per head the row kernel visits (16 keys at
+ *                d = 128, 32 at d = 64) that hold at least one visible key;
+ * and prices them with a cost model of both kernels on MI355X, fitted to
+ * measured calls: a launch term plus the larger of a throughput term (the work
+ * of all B * H heads over the whole chip) and a critical-path term (the work of
+ * the busiest workgroup for the tile kernel, of the busiest query row for the
+ * row kernel):
+ *   kernel = 1 (row kernel) if its estimate is lower, else 0 (tile kernel).
+ * Source: STOF page, Méthodologie 1 (kernel selection by an analytic model from
+ * mask sparsity and sequence length).
+ * Output pointers other than kernel may be NULL.
+ * Errors: RF_ERR_INVALID_ARG (NULL kernel, negative sizes, bits without
+ * kinds), RF_ERR_UNSUPPORTED (d not 64 or 128).
+ */
+int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B, int H, int Lq, int Lk, int d,
+                      int causal, int* kernel, double* est_tile_us, double* est_row_us, int64_t* tile_work,
+                      int64_t* row_groups);
+
+/*
  * Bytes of device workspace that rf_attention_decode_splitkv needs:
  * B*H*num_splits*(d + 1) fp32 values (normalised partial outputs and their
  * LSE), rounded up to 256 bytes. Returns 0 for invalid arguments.
@@ -302,7 +348,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 5
+#define RF_ABI_VERSION 6
 int rf_abi_version(void);
 
 #ifdef __cplusplus

@@ -19,7 +19,7 @@ __all__ = [
     "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_fwd_mod",
     "rf_attention_decode_splitkv",
     "rf_attention_decode_splitkv_workspace_size", "rf_attention_decode_gqa", "rf_attention_decode_gqa_workspace_size",
-    "rf_lse_merge", "rf_moe_route", "rf_abi_version",
+    "rf_lse_merge", "rf_moe_route", "rf_attention_fwd_rowwise", "rf_attention_plan", "rf_abi_version",
 ]
 
 RF_F32, RF_BF16 = 0, 1
@@ -63,6 +63,8 @@ def load():
         "rf_attention_decode_gqa": ([P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
         "rf_moe_route": ([P, P, P, I64, I, I, I, I, P], I),
+        "rf_attention_fwd_rowwise": ([P, P, P, P, P, I, I, I, I, I, F, I, P, P, I, P], I),
+        "rf_attention_plan": ([P, P, I, I, I, I, I, I, P, P, P, P, P], I),
         "rf_status_string": ([I], ctypes.c_char_p),
         "rf_last_error_message": ([], ctypes.c_char_p),
         "rf_abi_version": ([], I),
@@ -381,3 +383,50 @@ def rf_moe_route(logits, k, renorm=True, out_idx=None, out_w=None):
                           _stream(dev))
     _check(st, "rf_moe_route")
     return idx, w
+
+
+def rf_attention_fwd_rowwise(q, k, v, tile_kind=None, tile_bits=None, scale=None, causal=False, out=None, lse=None,
+                             want_lse=True):
+    """Row-wise masked attention (bf16): the result of rf_attention_fwd_bitmap by the row kernel.
+    tile_kind uint8 [ceil(Lq/64), ceil(Lk/64)] and tile_bits int64/uint64 [.., .., 64] on the GPU, or None."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError("k, v must be [B, H, Lk, d] matching q")
+    nI, nJ = math.ceil(Lq / MASK_TILE), math.ceil(Lk / MASK_TILE)
+    if tile_kind is not None and (tile_kind.dtype != torch.uint8 or tuple(tile_kind.shape) != (nI, nJ)):
+        raise ValueError(f"tile_kind must be uint8 {(nI, nJ)}")
+    if tile_bits is not None and (tile_bits.element_size() != 8 or tuple(tile_bits.shape) != (nI, nJ, MASK_TILE)):
+        raise ValueError(f"tile_bits must be 64-bit {(nI, nJ, MASK_TILE)}")
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    dev = _dev(q, k, v, o, lse, tile_kind, tile_bits)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.rf_attention_fwd_rowwise(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lq, Lk, d, float(scale),
+                                      1 if causal else 0, _ptr(tile_kind), _ptr(tile_bits), _dtype_code(q),
+                                      _stream(dev))
+    _check(st, "rf_attention_fwd_rowwise")
+    return o, lse
+
+
+def rf_attention_plan(tile_kind, tile_bits, B, H, Lq, Lk, d, causal):
+    """The analytic kernel choice from HOST (numpy) copies of a mask (either may be None).
+    Returns dict(kernel="tile"|"row", est_tile_us, est_row_us, tile_work, row_groups)."""
+    import numpy as np
+    lib = load()
+    kinds = None if tile_kind is None else np.ascontiguousarray(tile_kind, dtype=np.uint8)
+    bits = None if tile_bits is None else np.ascontiguousarray(tile_bits).view(np.uint64)
+    kern, et, er = ctypes.c_int(0), ctypes.c_double(0), ctypes.c_double(0)
+    tw, rg = ctypes.c_int64(0), ctypes.c_int64(0)
+    hp = lambda a: ctypes.c_void_p(0) if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.rf_attention_plan(hp(kinds), hp(bits), B, H, Lq, Lk, d, 1 if causal else 0, ctypes.byref(kern),
+                               ctypes.byref(et), ctypes.byref(er), ctypes.byref(tw), ctypes.byref(rg))
+    _check(st, "rf_attention_plan")
+    return dict(kernel="row" if kern.value == 1 else "tile", est_tile_us=et.value, est_row_us=er.value,
+                tile_work=tw.value, row_groups=rg.value)

@@ -29,6 +29,7 @@ SOURCES = [
     "attention_f32.hip",
     "attention_bf16.hip",
     "moe_route.hip",
+    "attention_rowwise.hip",
 ]
 
 COMMON = [

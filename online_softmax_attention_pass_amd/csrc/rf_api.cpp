@@ -138,6 +138,133 @@ int rf_layernorm_rows(const void* x, const float* gamma, const float* beta, void
   }
 }
 
+int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                             int Lq, int Lk, int d, float scale, int causal, const uint8_t* tile_kind,
+                             const uint64_t* tile_bits, int dtype, void* stream) {
+  const char* name = "rf_attention_fwd_rowwise";
+  try {
+    if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0)
+      return fail(RF_ERR_INVALID_ARG, "%s: negative size (B=%d H=%d Lq=%d Lk=%d)", name, B, H, Lq, Lk);
+    if (d < 1) return fail(RF_ERR_INVALID_ARG, "%s: d = %d < 1", name, d);
+    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "%s: scale is not finite", name);
+    if (dtype != RF_BF16) return fail(RF_ERR_UNSUPPORTED, "%s: only bf16 is supported", name);
+    if (d != 64 && d != 128) return fail(RF_ERR_UNSUPPORTED, "%s: d must be 64 or 128, got %d", name, d);
+    int64_t nq = 1, nk = 1;
+    if (!mul_ok(nq, B) || !mul_ok(nq, H) || !mul_ok(nq, Lq) || !mul_ok(nq, d) || !mul_ok(nq, 2) ||
+        !mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, 2))
+      return fail(RF_ERR_INVALID_ARG, "%s: tensor size overflows int64", name);
+    if (int64_t(B) * H * Lq == 0) return ok();
+    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL q or o", name);
+    if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "%s: NULL k or v", name);
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+      return fail(RF_ERR_UNSUPPORTED, "%s: needs 16-byte aligned q, k, v and o", name);
+    if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "%s: lse misaligned", name);
+    if (tile_bits != nullptr && !aligned(tile_bits, 8))
+      return fail(RF_ERR_INVALID_ARG, "%s: tile_bits must be 8-byte aligned", name);
+    if (tile_bits != nullptr && Lk > 0 && tile_kind == nullptr)
+      return fail(RF_ERR_INVALID_ARG, "%s: NULL tile_kind", name);
+    return hip_status(rf::launch_attention_rowwise(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, tile_kind,
+                                                   tile_bits, static_cast<hipStream_t>(stream)),
+                      name);
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
+  }
+}
+
+// Cost model of the two masked kernels on MI355X, in microseconds per call
+// (fitted to measured calls of both kernels over masks of many densities):
+//   tile kernel: a launch term, plus a term per 64 x 64 tile of MFMA work,
+//   row kernel : a launch term, plus a term per query row, plus a term per key
+//                group the rows visit.
+namespace {
+// Cost of one masked call on MI355X, in microseconds: a launch term plus the
+// larger of a throughput term (all the work spread over the chip) and a
+// critical-path term (the busiest workgroup of the tile kernel, the busiest
+// query row of the row kernel), the latter deciding when there are too few
+// workgroups or rows to fill 256 compute units. Fitted to bf16 calls of both
+// kernels over causal square masks (1k-8k) and non-causal short-query masks
+// (64-256 queries over 4k-16k keys), 1-50% of tiles and 1-50% of bits kept.
+struct PlanCost {
+  double tile_launch, tile_per_tile, tile_per_wg_tile;   // us, us per tile unit, us per tile unit of one workgroup
+  double row_launch, row_per_group, row_per_row_group;   // us, us per key group, us per key group of one row
+};
+PlanCost plan_cost(int d) {
+  if (d == 128) return {11.0, 3.94e-3, 0.96, 11.0, 4.6e-4, 0.585};
+  return {10.0, 2.87e-3, 1.64, 12.0, 4.6e-4, 0.585};
+}
+}  // namespace
+
+int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B, int H, int Lq, int Lk, int d,
+                      int causal, int* kernel, double* est_tile_us, double* est_row_us, int64_t* tile_work,
+                      int64_t* row_groups) {
+  const char* name = "rf_attention_plan";
+  try {
+    if (kernel == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL kernel", name);
+    if (B < 0 || H < 0 || Lq < 0 || Lk < 0)
+      return fail(RF_ERR_INVALID_ARG, "%s: negative size (B=%d H=%d Lq=%d Lk=%d)", name, B, H, Lq, Lk);
+    if (d != 64 && d != 128) return fail(RF_ERR_UNSUPPORTED, "%s: d must be 64 or 128, got %d", name, d);
+    if (tile_bits != nullptr && tile_kind == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL tile_kind", name);
+    const int n_ct = (Lk + 63) / 64;
+    const int64_t off = int64_t(Lk) - Lq;
+    const int bm = d == 128 ? 128 : 64;        // query rows per tile-kernel workgroup
+    const int kpi = d == 128 ? 16 : 32;        // keys per row-kernel group
+    auto kind_at = [&](int I, int J) -> int { return tile_kind == nullptr ? 1 : tile_kind[int64_t(I) * n_ct + J]; };
+    // tile kernel: per workgroup, the tiles any of its rows needs, each worth bm / 64 tiles of work
+    double tiles = 0.0, wg_max = 0.0;
+    for (int q0 = 0; q0 < Lq; q0 += bm) {
+      double wg_tiles = 0.0;
+      const int q1 = q0 + bm < Lq ? q0 + bm : Lq;
+      int64_t last = causal ? int64_t(q1 - 1) + off : int64_t(Lk) - 1;
+      if (last > Lk - 1) last = Lk - 1;
+      const int j_end = last < 0 ? 0 : int(last / 64) + 1;
+      for (int J = 0; J < j_end; ++J) {
+        bool any = false;
+        for (int I = q0 / 64; I <= (q1 - 1) / 64; ++I) any |= kind_at(I, J) != 0;
+        if (any) wg_tiles += bm / 64;
+      }
+      tiles += wg_tiles;
+      wg_max = wg_tiles > wg_max ? wg_tiles : wg_max;
+    }
+    // row kernel: per row, the key groups holding a visible key
+    double groups = 0.0, row_max = 0.0;
+    for (int i = 0; i < Lq; ++i) {
+      double row_groups_i = 0.0;
+      int64_t last = causal ? int64_t(i) + off : int64_t(Lk) - 1;
+      if (last > Lk - 1) last = Lk - 1;
+      const int j_end = last < 0 ? 0 : int(last / 64) + 1;
+      for (int J = 0; J < j_end; ++J) {
+        const int kind = kind_at(i / 64, J);
+        if (kind == 0) continue;
+        uint64_t word = (tile_bits != nullptr && kind != 1) ? tile_bits[(int64_t(i / 64) * n_ct + J) * 64 + i % 64]
+                                                            : ~uint64_t(0);
+        if (int64_t(J) * 64 + 63 > last) word &= (uint64_t(1) << int(last - int64_t(J) * 64 + 1)) - 1;
+        for (int kk = 0; kk < 64; kk += kpi)
+          if ((word >> kk) & ((uint64_t(1) << kpi) - 1)) row_groups_i += 1;
+      }
+      groups += row_groups_i;
+      row_max = row_groups_i > row_max ? row_groups_i : row_max;
+    }
+    const double heads = double(B) * H;
+    const PlanCost c = plan_cost(d);
+    auto mx = [](double a, double b) { return a > b ? a : b; };
+    const double t_tile = c.tile_launch + mx(c.tile_per_tile * tiles * heads, c.tile_per_wg_tile * wg_max);
+    const double t_row = c.row_launch + mx(c.row_per_group * groups * heads, c.row_per_row_group * row_max);
+    *kernel = t_row < t_tile ? 1 : 0;
+    if (est_tile_us != nullptr) *est_tile_us = t_tile;
+    if (est_row_us != nullptr) *est_row_us = t_row;
+    if (tile_work != nullptr) *tile_work = int64_t(tiles);
+    if (row_groups != nullptr) *row_groups = int64_t(groups);
+    return ok();
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
+  }
+}
+
 int rf_moe_route(const void* logits, int32_t* topk_idx, float* topk_w, int64_t T, int E, int k, int renorm,
                  int dtype, void* stream) {
   const char* name = "rf_moe_route";

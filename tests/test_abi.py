@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 5
+    assert lib.rf_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -305,3 +305,99 @@ def test_moe_route_validation(lib, args, code):
     assert lib.rf_moe_route(*args, NUL) == code
     if code != OK:
         assert "rf_moe_route" in _msg(lib)
+
+
+# ---------------------------------------------------------------------------
+# the analytic kernel choice (host only)
+# ---------------------------------------------------------------------------
+
+def _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal):
+    """Brute-force work counts: tiles per tile-kernel workgroup and visible key groups per row."""
+    import numpy as np
+    bm, kpi = (128, 16) if d == 128 else (64, 32)
+    i = np.arange(Lq)[:, None]
+    j = np.arange(Lk)[None, :]
+    vis = np.ones((Lq, Lk), bool) if not causal else (j <= i + (Lk - Lq))
+    kind = np.ones((Lq, Lk), np.uint8) if kinds is None else kinds[i // 64, j // 64]
+    vis_k = vis & (kind != 0)
+    if bits is not None:
+        word = bits[i // 64, j // 64, i % 64]
+        bit = ((word >> (j % 64).astype(np.uint64)) & np.uint64(1)) == 1
+        vis_e = vis_k & ((kind == 1) | bit)
+    else:
+        vis_e = vis_k
+    tiles = 0
+    for q0 in range(0, Lq, bm):
+        rows = slice(q0, min(Lq, q0 + bm))
+        last = min(Lk - 1, (min(Lq, q0 + bm) - 1) + (Lk - Lq)) if causal else Lk - 1
+        for J in range(0, last // 64 + 1 if last >= 0 else 0):
+            if (kind[rows, J * 64:(J + 1) * 64] != 0).any():
+                tiles += bm // 64
+    groups = int(sum(vis_e[:, g:g + kpi].any(axis=1).sum() for g in range(0, Lk, kpi)))
+    return tiles, groups
+
+
+@pytest.mark.parametrize("Lq,Lk,d,causal", [(300, 500, 128, True), (300, 500, 64, True), (130, 700, 128, False),
+                                           (64, 2048, 64, True), (1, 200, 128, True)])
+def test_plan_counts_match_brute_force(Lq, Lk, d, causal):
+    import numpy as np
+    r = np.random.default_rng(Lq + Lk + d)
+    nI, nJ = -(-Lq // 64), -(-Lk // 64)
+    kinds = r.choice([0, 1, 2, 5], size=(nI, nJ), p=[0.4, 0.2, 0.3, 0.1]).astype(np.uint8)
+    bits = (r.integers(0, 2 ** 62, size=(nI, nJ, 64), dtype=np.uint64) & r.integers(0, 2 ** 62, size=(nI, nJ, 64),
+                                                                                    dtype=np.uint64))
+    p = rf.rf_attention_plan(kinds, bits, 2, 3, Lq, Lk, d, causal)
+    assert (p["tile_work"], p["row_groups"]) == _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal)
+    p0 = rf.rf_attention_plan(None, None, 1, 1, Lq, Lk, d, causal)     # dense
+    assert (p0["tile_work"], p0["row_groups"]) == _plan_counts_numpy(None, None, Lq, Lk, d, causal)
+
+
+def test_plan_choices_at_the_extremes():
+    import numpy as np
+    # dense causal prefill: the tile kernel
+    assert rf.rf_attention_plan(None, None, 4, 32, 4096, 4096, 128, True)["kernel"] == "tile"
+    # a few scattered keys per row over long keys: the row kernel
+    Lq, Lk = 256, 16384
+    nI, nJ = Lq // 64, Lk // 64
+    kinds = np.full((nI, nJ), 2, np.uint8)
+    bits = np.zeros((nI, nJ, 64), np.uint64)
+    r = np.random.default_rng(5)
+    for I in range(nI):
+        for rr in range(64):
+            for J in r.choice(nJ, 4, replace=False):
+                bits[I, J, rr] |= np.uint64(1) << np.uint64(r.integers(64))
+    p = rf.rf_attention_plan(kinds, bits, 1, 8, Lq, Lk, 128, False)
+    assert p["kernel"] == "row" and p["est_row_us"] < p["est_tile_us"]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((NUL, NUL, 1, 1, 64, 64, 128, 1, NUL, NUL, NUL, NUL, NUL), INVALID),     # NULL kernel out
+    ((NUL, FAKE, 1, 1, 64, 64, 128, 1, "k", NUL, NUL, NUL, NUL), INVALID),    # bits without kinds
+    ((NUL, NUL, 1, 1, 64, 64, 96, 1, "k", NUL, NUL, NUL, NUL), UNSUP),
+    ((NUL, NUL, -1, 1, 64, 64, 128, 1, "k", NUL, NUL, NUL, NUL), INVALID),
+])
+def test_plan_validation(lib, args, code):
+    kern = ctypes.c_int(0)
+    args = tuple(ctypes.byref(kern) if a == "k" else a for a in args)
+    assert lib.rf_attention_plan(*args) == code
+
+
+ROW = dict(ATT, kinds=NUL, bits=NUL)
+
+
+def att_row(lib, **kw):
+    a = dict(ROW, **kw)
+    return lib.rf_attention_fwd_rowwise(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"], a["Lk"],
+                                        a["d"], a["scale"], a["causal"], a["kinds"], a["bits"], a["dtype"], NUL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=9), INVALID), (dict(B=-1), INVALID), (dict(d=0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(q=NUL), INVALID), (dict(k=NUL), INVALID),
+    (dict(o=P(0x10008)), UNSUP), (dict(bits=FAKE), INVALID), (dict(bits=P(0x10004), kinds=FAKE), INVALID),
+    (dict(B=0), OK), (dict(Lq=0), OK),
+])
+def test_rowwise_validation(lib, kw, code):
+    assert att_row(lib, **kw) == code
+    if code != OK:
+        assert "rf_attention_fwd_rowwise" in _msg(lib)
