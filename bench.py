@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "sparse": "attention_bf16.hip", "attn_f32": "attention_f32.hip", "bitmap": "attention_bf16.hip",
     "layernorm": "layernorm_rows.hip", "gqa": "attention_bf16.hip", "mla": "attention_bf16.hip",
     "alibi": "attention_bf16.hip", "softcap": "attention_bf16.hip", "window": "attention_bf16.hip",
-    "moe": "moe_route.hip",
+    "moe": "moe_route.hip", "bigbird": "attention_rowwise.hip",
 }
 
 
@@ -234,6 +234,38 @@ def setup_bitmap(rf, torch, W):
                        "visible_fraction_of_active": round(visible / (active * 64 * 64), 4)})
 
 
+def setup_bigbird(rf, torch, W):
+    """Extension workload: the row kernel on a chunk of 256 queries over 16384
+    keys under a BigBird-style element mask (the kernel the analytic choice
+    picks there); the tile kernel on the same call is timed beside it.
+    Algorithmic bytes: q, o and lse, the K and V rows of every key some query
+    row of the head sees (each once), and the mask words the rows read."""
+    c = W.EXTENSION_CONFIGS["bigbird_chunk"]
+    B, H, Lq, Lk, d = c["B"], c["H"], c["Lq"], c["Lk"], c["d"]
+    q = torch.from_numpy(W.normal_tensor(c["seed"], W.TID_Q, B, H, Lq, d, "bf16").view(np.int16)).view(
+        torch.bfloat16).cuda()
+    k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, B, H, Lk, d, "bf16").view(np.int16)).view(
+        torch.bfloat16).cuda() for t in (W.TID_K, W.TID_V))
+    vis = W.bigbird_chunk_mask(c["seed"], Lq, Lk, c["n_global"], c["window"], c["n_random"])
+    kinds, bits = W.element_mask_tiles(vis)
+    plan = rf.rf_attention_plan(kinds, bits, B, H, Lq, Lk, d, c["causal"])
+    kd = torch.from_numpy(kinds).cuda()
+    bd = torch.from_numpy(bits.view(np.int64)).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device="cuda")
+    keys = int(vis.any(axis=0).sum())
+    mask_bytes = kinds.size + 8 * Lq * int((kinds == 2).sum(axis=1).max(initial=0))
+    nbytes = B * H * (2 * Lq * d * 2 + Lq * 4 + keys * 2 * d * 2) + mask_bytes
+    return dict(fn=lambda: rf.rf_attention_fwd_rowwise(q, k, v, kd, bd, scale=c["scale"], causal=c["causal"],
+                                                       out=o, lse=lse),
+                alternatives={"tile_kernel": lambda: rf.rf_attention_fwd_bitmap(q, k, v, kd, bd, scale=c["scale"],
+                                                                                causal=c["causal"], out=o,
+                                                                                lse=lse)},
+                work=nbytes, unit="GB/s", bound="hbm", keep=(q, k, v, kd, bd, o, lse), cfg=c,
+                extra={"visible_per_row": int(vis.sum(axis=1).max()), "keys_seen_per_head": keys,
+                       "plan": {k_: (round(v_, 1) if isinstance(v_, float) else v_) for k_, v_ in plan.items()}})
+
+
 def setup_decode(rf, torch, W):
     c = W.CONFIGS[4]
     B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
@@ -336,7 +368,7 @@ def setup_copy(rf, torch, W):
 
 
 SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layernorm, "softmax": setup_softmax, "prefill": setup_prefill, "decode": setup_decode, "sparse": setup_sparse, "gqa": setup_gqa_decode, "mla": setup_mla_decode,
-          "alibi": setup_alibi, "softcap": setup_softcap, "window": setup_window, "moe": setup_moe,
+          "alibi": setup_alibi, "bigbird": setup_bigbird, "softcap": setup_softcap, "window": setup_window, "moe": setup_moe,
           "attn_f32": setup_attn_f32}
 
 
@@ -375,7 +407,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads",
-                    default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe")
+                    default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe,bigbird")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -422,6 +454,11 @@ def main():
         if merge_ms is not None:
             r["merge_ms"] = round(merge_ms, 5)
             r["partial_kernel_ms"] = round(kern_ms, 5)
+        for alt, fn in s.get("alternatives", {}).items():
+            for _ in range(args.warmup):
+                fn()
+            aper, _ = timer.run(fn, args.steps)
+            r[f"{alt}_ms"] = round(float(np.mean(aper)), 5)
         if "flops" in s:
             r["tflops"] = round(s["flops"] / (call_ms * 1e-3) / 1e12, 3)
         r.update(s.get("extra", {}))

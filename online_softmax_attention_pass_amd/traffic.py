@@ -44,6 +44,7 @@ KERNELS = {
     "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
     "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2>", "attention_bf16.hip"),
     "moe": ("moe_route_kernel", "moe_route.hip"),
+    "bigbird": ("attention_rowwise_kernel", "attention_rowwise.hip"),
 }
 COPY_KEY = "MulFunctor"
 COPY_BYTES = float(1 << 30)

@@ -198,6 +198,39 @@ def test_extension_bitmap_full_size(rf_gpu):
     _report("extension bitmap", e_o, e_l)
 
 
+def test_extension_bigbird_chunk_full_size(rf_gpu):
+    """256 queries over 16384 keys under a BigBird-style element mask (64
+    global keys, a 256-key causal window, 64 random keys per row), by the row
+    kernel and by the tile kernel: sampled heads and rows against the oracle,
+    and the two kernels against each other on every row."""
+    import torch
+    c = W.EXTENSION_CONFIGS["bigbird_chunk"]
+    B, H, Lq, Lk, d = c["B"], c["H"], c["Lq"], c["Lk"], c["d"]
+    q = W.normal_tensor(c["seed"], W.TID_Q, B, H, Lq, d, "bf16")
+    k, v = (W.normal_tensor(c["seed"], t, B, H, Lk, d, "bf16") for t in (W.TID_K, W.TID_V))
+    vis = W.bigbird_chunk_mask(c["seed"], Lq, Lk, c["n_global"], c["window"], c["n_random"])
+    kinds, bits = W.element_mask_tiles(vis)
+    assert rf_gpu.rf_attention_plan(kinds, bits, B, H, Lq, Lk, d, c["causal"])["kernel"] == "row"
+    note("extension bigbird chunk full size")
+    args = (dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(kinds).cuda(),
+            torch.from_numpy(bits.view(np.int64)).cuda())
+    o, lse = rf_gpu.rf_attention_fwd_rowwise(*args, scale=c["scale"], causal=c["causal"])
+    _same_again((o, lse), rf_gpu.rf_attention_fwd_rowwise(*args, scale=c["scale"], causal=c["causal"]), "rowwise")
+    ot, lt = rf_gpu.rf_attention_fwd_bitmap(*args, scale=c["scale"], causal=c["causal"])
+    got_o, got_l = host_f64(o), host_f64(lse)
+    rows = [0, 1, 63, 64, 127, 128, 200, 255]
+    e_o = e_l = 0.0
+    for h in (0, 17, 31):
+        ref_o, ref_lse = O.attention(*(O.bf16_bits_to_f64(a[:, h:h + 1]) for a in (q, k, v)), c["scale"],
+                                     c["causal"], kinds, q_rows=rows, tile_bits=bits)
+        e_o = max(e_o, assert_close(got_o[:, h:h + 1, rows], ref_o, 1e-2, "bigbird O"))
+        e_l = max(e_l, assert_close(got_l[:, h:h + 1, rows], ref_lse, 1e-3, "bigbird LSE"))
+    assert np.all(np.isfinite(got_l))
+    assert_close(got_o, host_f64(ot), 1e-2, "row vs tile O")
+    assert_close(got_l, host_f64(lt), 1e-3, "row vs tile LSE")
+    _report("extension bigbird chunk", e_o, e_l)
+
+
 def test_extension_layernorm_full_size(rf_gpu):
     """Layer normalisation of fp32 4096 x 32768 (the softmax workload's shape):
     sampled rows against the oracle, every row's statistics cheaply."""

@@ -220,6 +220,13 @@ EXTENSION_CONFIGS = {
     "score_mod": dict(name="score_mod_bf16_B4_H32_L4096_d128", kind="attention", dtype="bf16", B=4, H=32,
                       Lq=4096, Lk=4096, d=128, scale=1.0 / math.sqrt(128), causal=True, softcap=50.0,
                       window=1024, seed=10),
+    # A chunk of 256 queries at the end of a 16384-key context under a
+    # BigBird-style element mask (STOF's mask family): 64 global keys, a causal
+    # local window of 256 keys, and 64 keys per row drawn uniformly at random
+    # from the rest of the row's past: the highly sparse, short-query regime.
+    "bigbird_chunk": dict(name="bigbird_chunk_bf16_B1_H32_Lq256_Lk16384_d128", kind="attention", dtype="bf16",
+                          B=1, H=32, Lq=256, Lk=16384, d=128, scale=1.0 / math.sqrt(128), causal=True,
+                          n_global=64, window=256, n_random=64, seed=12),
     # Mixture-of-experts routing: router logits of 131072 tokens over 256
     # experts, top 8 renormalised (a large-expert-count layer).
     "moe": dict(name="moe_route_f32_T131072_E256_k8", kind="moe", dtype="f32", T=131072, E=256, k=8, renorm=True,
@@ -274,3 +281,41 @@ def config_block_mask(cfg: int):
         return None
     n = math.ceil(c["Lq"] / MASK_TILE)
     return window_random_block_mask(cfg, n, window_tiles=512 // MASK_TILE, frac=0.10)
+
+
+def element_mask_tiles(vis: np.ndarray):
+    """Tile kinds uint8 [nI, nJ] and row bitmaps uint64 [nI, nJ, 64] of a
+    boolean element mask vis [Lq, Lk] (True = visible): kind 0 for a tile with
+    no visible element, 1 for one whose elements inside [Lq, Lk] are all
+    visible, 2 otherwise, with word r holding row r's 64 keys (bit j)."""
+    Lq, Lk = vis.shape
+    nI, nJ = math.ceil(Lq / MASK_TILE), math.ceil(Lk / MASK_TILE)
+    pad = np.zeros((nI * MASK_TILE, nJ * MASK_TILE), bool)
+    pad[:Lq, :Lk] = vis
+    inside = np.zeros_like(pad)
+    inside[:Lq, :Lk] = True
+    t = pad.reshape(nI, MASK_TILE, nJ, MASK_TILE).transpose(0, 2, 1, 3)
+    tin = inside.reshape(nI, MASK_TILE, nJ, MASK_TILE).transpose(0, 2, 1, 3)
+    anyv = t.any(axis=(2, 3))
+    allv = (t | ~tin).all(axis=(2, 3))
+    kinds = np.where(allv & anyv, 1, np.where(anyv, 2, 0)).astype(np.uint8)
+    weights = np.uint64(1) << np.arange(MASK_TILE, dtype=np.uint64)
+    bits = (t.astype(np.uint64) * weights).sum(axis=3, dtype=np.uint64)
+    bits[kinds != 2] = 0
+    return np.ascontiguousarray(kinds), np.ascontiguousarray(bits)
+
+
+def bigbird_chunk_mask(seed: int, Lq: int, Lk: int, n_global: int, window: int, n_random: int) -> np.ndarray:
+    """Boolean element mask [Lq, Lk] for Lq queries at positions Lk - Lq + i:
+    keys j < n_global, keys in (p - window, p], and n_random keys per row drawn
+    without replacement from [n_global, p - window] (all of them if fewer)."""
+    vis = np.zeros((Lq, Lk), bool)
+    for i in range(Lq):
+        p = Lk - Lq + i
+        vis[i, :min(n_global, p + 1)] = True
+        vis[i, max(0, p - window + 1):p + 1] = True
+        lo, hi = n_global, p - window + 1
+        if hi > lo:
+            pick = rng(seed, TID_MASK, i).choice(hi - lo, size=min(n_random, hi - lo), replace=False)
+            vis[i, lo + pick] = True
+    return vis
