@@ -80,7 +80,9 @@ def log(msg):
 
 
 class Timer:
-    """Per-call HIP events on the current stream."""
+    """HIP events on the current stream: one pair around all the timed calls
+    (the launches queue back to back, so the mean is the kernels' own time),
+    then one pair per call in a second pass for the spread."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -88,17 +90,24 @@ class Timer:
     def run(self, fn, steps):
         torch = self.torch
         stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for a, b in ev:
-            a.record(stream)
+        a.record(stream)
+        for _ in range(steps):
             fn()
-            b.record(stream)
+        b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        per = [a.elapsed_time(b) for a, b in ev]
-        return per, wall
+        mean_ms = a.elapsed_time(b) / steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for x, y in ev:
+            x.record(stream)
+            fn()
+            y.record(stream)
+        torch.cuda.synchronize()
+        per = [x.elapsed_time(y) for x, y in ev]
+        return mean_ms, per, wall
 
 
 def roofline(bound, achieved, peak, unit, traffic):
@@ -404,8 +413,8 @@ def cpu_baseline_softmax(W, budget_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workloads",
                     default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe,bigbird")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -434,15 +443,13 @@ def main():
             s["fn"]()
         torch.cuda.synchronize()
         log(f"{name}: timing {args.steps} calls")
-        per, wall = timer.run(s["fn"], args.steps)
-        call_ms = float(np.mean(per))
+        call_ms, per, wall = timer.run(s["fn"], args.steps)
         kern_ms = call_ms
         merge_ms = None
         if "subtract" in s:
             for _ in range(args.warmup):
                 s["subtract"]()
-            mper, _ = timer.run(s["subtract"], args.steps)
-            merge_ms = float(np.mean(mper))
+            merge_ms, _, _ = timer.run(s["subtract"], args.steps)
             kern_ms = call_ms - merge_ms
         thr = s["work"] / (call_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
         kthr = s["work"] / (kern_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
@@ -457,8 +464,7 @@ def main():
         for alt, fn in s.get("alternatives", {}).items():
             for _ in range(args.warmup):
                 fn()
-            aper, _ = timer.run(fn, args.steps)
-            r[f"{alt}_ms"] = round(float(np.mean(aper)), 5)
+            r[f"{alt}_ms"] = round(timer.run(fn, args.steps)[0], 5)
         if "flops" in s:
             r["tflops"] = round(s["flops"] / (call_ms * 1e-3) / 1e12, 3)
         r.update(s.get("extra", {}))
