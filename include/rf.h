@@ -231,8 +231,9 @@ int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* 
  *   tile_work  : 64 x 64 tiles of matrix-core work per head, i.e. for every
  *                workgroup of query rows (128 rows at d = 128, 64 at d = 64)
  *                the key tiles any of its rows needs, times rows / 64;
- *   row_groups : key groups per head the row kernel visits (16 keys at
- *                d = 128, 32 at d = 64) that hold at least one visible key;
+ *   row_batches: batches per head the row kernel processes, each up to
+ *                16 visible keys of one row at d = 128 (32 at d = 64), i.e.
+ *                the sum over rows of ceil(visible keys / batch size);
  * and prices them with a cost model of both kernels on MI355X, fitted to
  * measured calls: a launch term plus the larger of a throughput term (the work
  * of all B * H heads over the whole chip) and a critical-path term (the work of
@@ -247,7 +248,7 @@ int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* 
  */
 int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B, int H, int Lq, int Lk, int d,
                       int causal, int* kernel, double* est_tile_us, double* est_row_us, int64_t* tile_work,
-                      int64_t* row_groups);
+                      int64_t* row_batches);
 
 /*
  * Bytes of device workspace that rf_attention_decode_splitkv needs:

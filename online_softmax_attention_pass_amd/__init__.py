@@ -417,7 +417,7 @@ def rf_attention_fwd_rowwise(q, k, v, tile_kind=None, tile_bits=None, scale=None
 
 def rf_attention_plan(tile_kind, tile_bits, B, H, Lq, Lk, d, causal):
     """The analytic kernel choice from HOST (numpy) copies of a mask (either may be None).
-    Returns dict(kernel="tile"|"row", est_tile_us, est_row_us, tile_work, row_groups)."""
+    Returns dict(kernel="tile"|"row", est_tile_us, est_row_us, tile_work, row_batches)."""
     import numpy as np
     lib = load()
     kinds = None if tile_kind is None else np.ascontiguousarray(tile_kind, dtype=np.uint8)
@@ -429,4 +429,4 @@ def rf_attention_plan(tile_kind, tile_bits, B, H, Lq, Lk, d, causal):
                                ctypes.byref(et), ctypes.byref(er), ctypes.byref(tw), ctypes.byref(rg))
     _check(st, "rf_attention_plan")
     return dict(kernel="row" if kern.value == 1 else "tile", est_tile_us=et.value, est_row_us=er.value,
-                tile_work=tw.value, row_groups=rg.value)
+                tile_work=tw.value, row_batches=rg.value)

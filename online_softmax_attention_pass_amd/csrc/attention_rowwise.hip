@@ -16,6 +16,7 @@
 
 #include "launch.h"
 #include "rf_internal.h"
+#include "rows_io.h"
 
 namespace rf {
 namespace {
@@ -32,24 +33,37 @@ template <int D, int U>
 __global__ __launch_bounds__(256) void attention_rowwise_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float scale_log2, int causal,
-    const uint8_t* __restrict__ tile_kind, const uint64_t* __restrict__ tile_bits, int64_t n_rows) {
+    const uint8_t* __restrict__ tile_kind, const uint64_t* __restrict__ tile_bits, int64_t n_rows,
+    int xcd_remap) {
   constexpr int LPK = D / 8;     // lanes per key
   constexpr int KPW = 64 / LPK;  // keys per load step
-  constexpr int KPI = KPW * U;   // keys per iteration
-  static_assert(kRowTile % KPI == 0, "iterations tile the 64-key tile");
+  constexpr int KB = KPW * U;    // keys per batch
+  static_assert(KB <= 32, "a batch fits the ring with a tile's worth of room");
+  __shared__ int s_pend[4][64];  // per wave: the ring of pending visible keys
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int sub = lane / LPK;  // which key of a load step
   const int ds = lane % LPK;   // this lane's 8-element slice of d
+  int* pend = s_pend[wave];
   const int n_cols = (Lk + kRowTile - 1) / kRowTile;
   const int64_t off = int64_t(Lk) - Lq;  // bottom-right causal alignment
 
-  for (int64_t row = int64_t(blockIdx.x) * 4 + wave; row < n_rows; row += int64_t(gridDim.x) * 4) {
+  // The hardware deals consecutive workgroups to the 8 XCDs in turn; with
+  // xcd_remap, XCD x takes the x-th eighth of the rows instead, so the rows of
+  // a head run on one XCD and its L2 serves the keys they share (window and
+  // global keys).
+  const int64_t n_wg = gridDim.x;
+  const int64_t blk = xcd_remap ? (blockIdx.x % 8) * (n_wg / 8) + blockIdx.x / 8 : int64_t(blockIdx.x);
+  for (int64_t row = blk * 4 + wave; row < n_rows; row += n_wg * 4) {
     const int64_t bh = row / Lq;
     const int i = int(row % Lq);
     const uint4 qv = *reinterpret_cast<const uint4*>(q + row * D + 8 * ds);
-    const uint16_t* kb = k + bh * int64_t(Lk) * D + 8 * ds;
-    const uint16_t* vb = v + bh * int64_t(Lk) * D + 8 * ds;
+    // K and V of the head as buffer resources: a hidden key's lanes load from
+    // an offset past the end, which reads 0 without touching memory, so every
+    // group issues the same loads and their count is known to the compiler.
+    const uint32_t head_bytes = uint32_t(Lk) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = row_rsrc(k + bh * int64_t(Lk) * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = row_rsrc(v + bh * int64_t(Lk) * D, head_bytes);
     // last visible key of the row (causal rule and sequence end)
     int64_t last = causal ? int64_t(i) + off : int64_t(Lk) - 1;
     if (last > Lk - 1) last = Lk - 1;
@@ -61,81 +75,126 @@ __global__ __launch_bounds__(256) void attention_rowwise_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-    // The row's mask, 64 tiles per step: lane j reads tile J0 + j's kind and
-    // this row's word of it, a ballot keeps the tiles with a visible key, and
-    // the wave visits just those (the word comes back by readlane).
-    for (int J0 = 0; J0 < j_end; J0 += 64) {
-      const int Jl = J0 + lane;
-      uint64_t wl = 0;
-      if (Jl < j_end) {
-        const uint8_t kind = tile_kind != nullptr ? tile_kind[mrow + Jl] : uint8_t(1);
-        if (kind != 0)
-          wl = (tile_bits != nullptr && kind != 1) ? tile_bits[(mrow + Jl) * kRowTile + (i % kRowTile)]
-                                                   : ~uint64_t(0);
-        if (int64_t(Jl) * kRowTile + kRowTile - 1 > last) {  // keys past the last visible one
-          const int n = int(last - int64_t(Jl) * kRowTile) + 1;  // 1 .. 63 (Jl < j_end)
-          wl &= (uint64_t(1) << n) - 1;
-        }
-      }
-      uint64_t todo = __builtin_amdgcn_ballot_w64(wl != 0);
-      while (todo != 0) {
-        const int jl = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(wl), jl);
-        const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(wl >> 32), jl);
-        const uint64_t word = (uint64_t(hi) << 32) | lo;
-        const int k0 = (J0 + jl) * kRowTile;
-        for (int kk = 0; kk < kRowTile; kk += KPI) {
-          if (((word >> kk) & ((uint64_t(1) << KPI) - 1)) == 0) continue;  // no visible key in this group
-          uint4 kr[U], vr[U];
-          bool vis[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int t = kk + u * KPW + sub;
-            vis[u] = (word >> t) & 1;
-            const int64_t key = k0 + t;
-            if (vis[u]) {
-              kr[u] = nt_load(reinterpret_cast<const uint4*>(kb + key * D));
-              vr[u] = nt_load(reinterpret_cast<const uint4*>(vb + key * D));
-            } else {
-              kr[u] = make_uint4(0, 0, 0, 0);
-              vr[u] = make_uint4(0, 0, 0, 0);
+    // The row's visible keys in order, gathered into batches of KB keys. The
+    // mask is read 64 tiles at a time: lane j reads tile J0 + j's kind and this
+    // row's word of it, and a ballot keeps the tiles with a visible key. Each
+    // such tile's word comes back to the whole wave by readlane, and its set
+    // bits are appended, in order, to this wave's list of pending keys in LDS
+    // (a 64-entry ring): lane j writes key k0 + j at its rank among the set bits.
+    int J0 = -kRowTile, k0 = 0, head = 0, n_pend = 0;
+    uint64_t wl = 0, todo = 0, word = 0;
+    auto fill = [&]() {
+      while (n_pend < KB) {
+        if (word == 0) {
+          if (todo == 0) {
+            J0 += 64;
+            if (J0 >= j_end) return;
+            const int Jl = J0 + lane;
+            wl = 0;
+            if (Jl < j_end) {
+              const uint8_t kind = tile_kind != nullptr ? tile_kind[mrow + Jl] : uint8_t(1);
+              if (kind != 0)
+                wl = (tile_bits != nullptr && kind != 1) ? tile_bits[(mrow + Jl) * kRowTile + (i % kRowTile)]
+                                                         : ~uint64_t(0);
+              if (int64_t(Jl) * kRowTile + kRowTile - 1 > last) {  // keys past the last visible one
+                const int n = int(last - int64_t(Jl) * kRowTile) + 1;  // 1 .. 63 (Jl < j_end)
+                wl &= (uint64_t(1) << n) - 1;
+              }
             }
+            todo = __builtin_amdgcn_ballot_w64(wl != 0);
+            continue;
           }
-          float ts[U];
-          float bm = kNegInf;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            float dsum = dot2_bf16r(kr[u].x, qv.x, 0.f);
-            dsum = dot2_bf16r(kr[u].y, qv.y, dsum);
-            dsum = dot2_bf16r(kr[u].z, qv.z, dsum);
-            dsum = dot2_bf16r(kr[u].w, qv.w, dsum);
-            dsum = group_sum<LPK>(dsum);
-            ts[u] = vis[u] ? dsum * scale_log2 : kNegInf;
-            bm = fmaxf(bm, ts[u]);
-          }
-          const float mn = fmaxf(m, bm);
-          const float mu = (mn == kNegInf) ? 0.f : mn;
-          const float alpha = fast_exp2(m - mu);
-          l *= alpha;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const float p = fast_exp2(ts[u] - mu);
-            l += p;
-            acc[0] += p * bf16_lo(vr[u].x);
-            acc[1] += p * bf16_hi(vr[u].x);
-            acc[2] += p * bf16_lo(vr[u].y);
-            acc[3] += p * bf16_hi(vr[u].y);
-            acc[4] += p * bf16_lo(vr[u].z);
-            acc[5] += p * bf16_hi(vr[u].z);
-            acc[6] += p * bf16_lo(vr[u].w);
-            acc[7] += p * bf16_hi(vr[u].w);
-          }
-          m = mn;
+          const int jl = __builtin_ctzll(todo);
+          todo &= todo - 1;
+          const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(wl), jl);
+          const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(wl >> 32), jl);
+          word = (uint64_t(hi) << 32) | lo;
+          k0 = (J0 + jl) * kRowTile;
         }
+        // Take as many of the tile's keys as the ring has room for.
+        const int rank = int(__builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u)));
+        const bool take = ((word >> lane) & 1) != 0 && rank < 64 - n_pend;
+        if (take) pend[(head + n_pend + rank) & 63] = k0 + lane;
+        const uint64_t taken = __builtin_amdgcn_ballot_w64(take);
+        n_pend += __builtin_popcountll(taken);
+        word &= ~taken;
       }
+    };
+    // The next batch: lane (u, sub) gets key u KPW + sub of it, or -1 past its
+    // end; returns the batch size (0 when the row is done).
+    auto take_batch = [&](int (&key)[U]) {
+      fill();
+      const int nb = n_pend < KB ? n_pend : KB;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sl = u * KPW + sub;
+        key[u] = sl < nb ? pend[(head + sl) & 63] : -1;
+      }
+      head = (head + nb) & 63;
+      n_pend -= nb;
+      return nb;
+    };
+    // Loads of one batch: this lane's 16 bytes of its key, or 0 (an offset past
+    // the end reads 0 without touching memory).
+    auto issue = [&](const int (&key)[U], uint4 (&kr)[U], uint4 (&vr)[U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t boff = key[u] >= 0 ? uint32_t(key[u]) * (D * 2) + 16u * uint32_t(ds) : 0x80000000u;
+        const buf_u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rk, int(boff), 0, kBufNonTemporal);
+        const buf_u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rv, int(boff), 0, kBufNonTemporal);
+        kr[u] = make_uint4(a[0], a[1], a[2], a[3]);
+        vr[u] = make_uint4(b[0], b[1], b[2], b[3]);
+      }
+    };
+    // The online update with one batch.
+    auto consume = [&](const int (&key)[U], const uint4 (&kr)[U], const uint4 (&vr)[U]) {
+      float ts[U];
+      float bm = kNegInf;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float dsum = dot2_bf16r(kr[u].x, qv.x, 0.f);
+        dsum = dot2_bf16r(kr[u].y, qv.y, dsum);
+        dsum = dot2_bf16r(kr[u].z, qv.z, dsum);
+        dsum = dot2_bf16r(kr[u].w, qv.w, dsum);
+        dsum = group_sum<LPK>(dsum);
+        ts[u] = key[u] >= 0 ? dsum * scale_log2 : kNegInf;
+        bm = fmaxf(bm, ts[u]);
+      }
+      const float mn = fmaxf(m, bm);
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m - mu);
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float p = fast_exp2(ts[u] - mu);
+        l += p;
+        acc[0] += p * bf16_lo(vr[u].x);
+        acc[1] += p * bf16_hi(vr[u].x);
+        acc[2] += p * bf16_lo(vr[u].y);
+        acc[3] += p * bf16_hi(vr[u].y);
+        acc[4] += p * bf16_lo(vr[u].z);
+        acc[5] += p * bf16_hi(vr[u].z);
+        acc[6] += p * bf16_lo(vr[u].w);
+        acc[7] += p * bf16_hi(vr[u].w);
+      }
+      m = mn;
+    };
+    // Two batches in flight: the next batch's loads go out before the current
+    // one is consumed (unrolled by two, so no register copies).
+    int key_a[U], key_b[U];
+    uint4 ka[U], va[U], kb2[U], vb2[U];
+    bool have_a = take_batch(key_a) > 0;
+    if (have_a) issue(key_a, ka, va);
+    while (have_a) {
+      const bool have_b = take_batch(key_b) > 0;
+      if (have_b) issue(key_b, kb2, vb2);
+      consume(key_a, ka, va);
+      if (!have_b) break;
+      have_a = take_batch(key_a) > 0;
+      if (have_a) issue(key_a, ka, va);
+      consume(key_b, kb2, vb2);
     }
     // Merge the KPW key groups of the wave (lanes with equal ds).
 #pragma unroll
@@ -172,6 +231,7 @@ hipError_t launch_attention_rowwise(const void* q, const void* k, const void* v,
   const int64_t n_rows = int64_t(B) * H * Lq;
   const int64_t blocks = (n_rows + 3) / 4;
   const unsigned grid = unsigned(blocks < (1 << 20) ? blocks : (1 << 20));
+  const int xcd_remap = grid % 8 == 0 ? 1 : 0;
   const float scale_log2 = float(double(scale) * 1.4426950408889634);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
@@ -179,10 +239,10 @@ hipError_t launch_attention_rowwise(const void* q, const void* k, const void* v,
   auto* oo = static_cast<uint16_t*>(o);
   if (d == 128)
     hipLaunchKernelGGL((attention_rowwise_kernel<128, 4>), dim3(grid), dim3(256), 0, stream, qq, kk, vv, oo, lse, Lq,
-                       Lk, scale_log2, causal, tile_kind, tile_bits, n_rows);
+                       Lk, scale_log2, causal, tile_kind, tile_bits, n_rows, xcd_remap);
   else
     hipLaunchKernelGGL((attention_rowwise_kernel<64, 4>), dim3(grid), dim3(256), 0, stream, qq, kk, vv, oo, lse, Lq,
-                       Lk, scale_log2, causal, tile_kind, tile_bits, n_rows);
+                       Lk, scale_log2, causal, tile_kind, tile_bits, n_rows, xcd_remap);
   return hipGetLastError();
 }
 

@@ -184,22 +184,25 @@ namespace {
 // larger of a throughput term (all the work spread over the chip) and a
 // critical-path term (the busiest workgroup of the tile kernel, the busiest
 // query row of the row kernel), the latter deciding when there are too few
-// workgroups or rows to fill 256 compute units. Fitted to bf16 calls of both
-// kernels over causal square masks (1k-8k) and non-causal short-query masks
-// (64-256 queries over 4k-16k keys), 1-50% of tiles and 1-50% of bits kept.
+// workgroups or rows to fill 256 compute units. Row-kernel work is its batches
+// of visible keys plus row_per_tile of a batch for every tile the row visits.
+// Fitted to bf16 calls of both kernels over causal square masks (1k-8k) and
+// non-causal short-query masks (64-256 queries over 4k-16k keys), 1-100% of
+// tiles and 1-50% of bits kept.
 struct PlanCost {
-  double tile_launch, tile_per_tile, tile_per_wg_tile;   // us, us per tile unit, us per tile unit of one workgroup
-  double row_launch, row_per_group, row_per_row_group;   // us, us per key group, us per key group of one row
+  double tile_launch, tile_per_tile, tile_per_wg_tile;  // us, us per tile unit, us per tile unit of one workgroup
+  double row_launch, row_per_batch, row_per_row_batch;  // us, us per batch, us per batch of one row
+  double row_per_tile;                                  // batches per visited tile
 };
 PlanCost plan_cost(int d) {
-  if (d == 128) return {11.0, 3.94e-3, 0.96, 11.0, 4.6e-4, 0.585};
-  return {10.0, 2.87e-3, 1.64, 12.0, 4.6e-4, 0.585};
+  if (d == 128) return {11.0, 3.94e-3, 0.96, 11.0, 6.08e-4, 5e-4, 0.25};
+  return {10.0, 2.87e-3, 1.64, 12.0, 8.35e-4, 0.854, 0.1};
 }
 }  // namespace
 
 int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B, int H, int Lq, int Lk, int d,
                       int causal, int* kernel, double* est_tile_us, double* est_row_us, int64_t* tile_work,
-                      int64_t* row_groups) {
+                      int64_t* row_batches) {
   const char* name = "rf_attention_plan";
   try {
     if (kernel == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL kernel", name);
@@ -210,7 +213,7 @@ int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B
     const int n_ct = (Lk + 63) / 64;
     const int64_t off = int64_t(Lk) - Lq;
     const int bm = d == 128 ? 128 : 64;        // query rows per tile-kernel workgroup
-    const int kpi = d == 128 ? 16 : 32;        // keys per row-kernel group
+    const int kb = d == 128 ? 16 : 32;         // visible keys per row-kernel batch
     auto kind_at = [&](int I, int J) -> int { return tile_kind == nullptr ? 1 : tile_kind[int64_t(I) * n_ct + J]; };
     // tile kernel: per workgroup, the tiles any of its rows needs, each worth bm / 64 tiles of work
     double tiles = 0.0, wg_max = 0.0;
@@ -228,35 +231,39 @@ int rf_attention_plan(const uint8_t* tile_kind, const uint64_t* tile_bits, int B
       tiles += wg_tiles;
       wg_max = wg_tiles > wg_max ? wg_tiles : wg_max;
     }
-    // row kernel: per row, the key groups holding a visible key
-    double groups = 0.0, row_max = 0.0;
+    // row kernel: per row, its batches of kb visible keys and the tiles it visits
+    const PlanCost c = plan_cost(d);
+    double batches = 0.0, row_work = 0.0, row_max = 0.0;
     for (int i = 0; i < Lq; ++i) {
-      double row_groups_i = 0.0;
       int64_t last = causal ? int64_t(i) + off : int64_t(Lk) - 1;
       if (last > Lk - 1) last = Lk - 1;
       const int j_end = last < 0 ? 0 : int(last / 64) + 1;
+      int64_t vis = 0, tiles_i = 0;
       for (int J = 0; J < j_end; ++J) {
         const int kind = kind_at(i / 64, J);
         if (kind == 0) continue;
         uint64_t word = (tile_bits != nullptr && kind != 1) ? tile_bits[(int64_t(i / 64) * n_ct + J) * 64 + i % 64]
                                                             : ~uint64_t(0);
         if (int64_t(J) * 64 + 63 > last) word &= (uint64_t(1) << int(last - int64_t(J) * 64 + 1)) - 1;
-        for (int kk = 0; kk < 64; kk += kpi)
-          if ((word >> kk) & ((uint64_t(1) << kpi) - 1)) row_groups_i += 1;
+        if (word == 0) continue;
+        vis += __builtin_popcountll(word);
+        tiles_i += 1;
       }
-      groups += row_groups_i;
-      row_max = row_groups_i > row_max ? row_groups_i : row_max;
+      const double b_i = double((vis + kb - 1) / kb);
+      const double w_i = b_i + c.row_per_tile * double(tiles_i);
+      batches += b_i;
+      row_work += w_i;
+      row_max = w_i > row_max ? w_i : row_max;
     }
     const double heads = double(B) * H;
-    const PlanCost c = plan_cost(d);
     auto mx = [](double a, double b) { return a > b ? a : b; };
     const double t_tile = c.tile_launch + mx(c.tile_per_tile * tiles * heads, c.tile_per_wg_tile * wg_max);
-    const double t_row = c.row_launch + mx(c.row_per_group * groups * heads, c.row_per_row_group * row_max);
+    const double t_row = c.row_launch + mx(c.row_per_batch * row_work * heads, c.row_per_row_batch * row_max);
     *kernel = t_row < t_tile ? 1 : 0;
     if (est_tile_us != nullptr) *est_tile_us = t_tile;
     if (est_row_us != nullptr) *est_row_us = t_row;
     if (tile_work != nullptr) *tile_work = int64_t(tiles);
-    if (row_groups != nullptr) *row_groups = int64_t(groups);
+    if (row_batches != nullptr) *row_batches = int64_t(batches);
     return ok();
   } catch (const std::exception& e) {
     return fail(RF_ERR_HIP, "%s: %s", name, e.what());

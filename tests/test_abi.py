@@ -312,9 +312,10 @@ def test_moe_route_validation(lib, args, code):
 # ---------------------------------------------------------------------------
 
 def _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal):
-    """Brute-force work counts: tiles per tile-kernel workgroup and visible key groups per row."""
+    """Brute-force work counts: tiles per tile-kernel workgroup, and per row the
+    batches of visible keys (16 at d = 128, 32 at d = 64) of the row kernel."""
     import numpy as np
-    bm, kpi = (128, 16) if d == 128 else (64, 32)
+    bm, kb = (128, 16) if d == 128 else (64, 32)
     i = np.arange(Lq)[:, None]
     j = np.arange(Lk)[None, :]
     vis = np.ones((Lq, Lk), bool) if not causal else (j <= i + (Lk - Lq))
@@ -333,8 +334,8 @@ def _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal):
         for J in range(0, last // 64 + 1 if last >= 0 else 0):
             if (kind[rows, J * 64:(J + 1) * 64] != 0).any():
                 tiles += bm // 64
-    groups = int(sum(vis_e[:, g:g + kpi].any(axis=1).sum() for g in range(0, Lk, kpi)))
-    return tiles, groups
+    batches = int(sum(-(-int(n) // kb) for n in vis_e.sum(axis=1)))
+    return tiles, batches
 
 
 @pytest.mark.parametrize("Lq,Lk,d,causal", [(300, 500, 128, True), (300, 500, 64, True), (130, 700, 128, False),
@@ -347,9 +348,9 @@ def test_plan_counts_match_brute_force(Lq, Lk, d, causal):
     bits = (r.integers(0, 2 ** 62, size=(nI, nJ, 64), dtype=np.uint64) & r.integers(0, 2 ** 62, size=(nI, nJ, 64),
                                                                                     dtype=np.uint64))
     p = rf.rf_attention_plan(kinds, bits, 2, 3, Lq, Lk, d, causal)
-    assert (p["tile_work"], p["row_groups"]) == _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal)
+    assert (p["tile_work"], p["row_batches"]) == _plan_counts_numpy(kinds, bits, Lq, Lk, d, causal)
     p0 = rf.rf_attention_plan(None, None, 1, 1, Lq, Lk, d, causal)     # dense
-    assert (p0["tile_work"], p0["row_groups"]) == _plan_counts_numpy(None, None, Lq, Lk, d, causal)
+    assert (p0["tile_work"], p0["row_batches"]) == _plan_counts_numpy(None, None, Lq, Lk, d, causal)
 
 
 def test_plan_choices_at_the_extremes():
