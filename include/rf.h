@@ -207,9 +207,9 @@ int rf_attention_fwd_mod(const void* q, const void* k, const void* v, void* o, f
  * Row-wise masked attention: exactly what rf_attention_fwd_bitmap computes
  * (causal rule, tile kinds, row bitmaps inside partial tiles), by the row
  * kernel of the dual-kernel strategy: one wavefront per query row walks only
- * the key tiles its mask row keeps and, inside them, only the groups of keys
- * with a visible one, with lane-level reductions and no synchronisation across
- * wavefronts. Suited to highly sparse masks on short sequences; the tile
+ * the key tiles its mask row keeps and loads and multiplies only their visible
+ * keys (in batches of 16 keys at d = 128, 32 at d = 64), with lane-level
+ * reductions and no synchronisation across wavefronts. Suited to highly sparse masks on short sequences; the tile
  * kernel (rf_attention_fwd_bitmap) to the rest. rf_attention_plan chooses.
  * Source: STOF page, Méthodologie 1 (dual-kernel strategy: row-wise kernel and
  * block-wise kernel, chosen by an analytic model).

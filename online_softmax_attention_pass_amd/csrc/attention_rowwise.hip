@@ -6,12 +6,13 @@
 // 64-bit row word per tile row (bit j: key j of the tile is visible).
 //
 // One wavefront owns one query row and walks only the key tiles its mask row
-// keeps, and inside a tile only the key groups with a visible key: a sparse
-// row costs its visible keys, not whole 64 x 64 tiles. Lanes are laid out as
-// in the split-KV decode kernel: D/8 lanes share a key (8 elements of d each,
-// 16-byte coalesced loads), KPW = 64 / (D/8) keys per load step, U steps per
-// iteration; each group of D/8 lanes keeps its own online (m, l, acc), and the
-// groups meet in the (m, l, acc) monoid at the end. Scores are in log2 units.
+// keeps; their visible keys, in order, are gathered into batches of KB keys,
+// so a sparse row costs its visible keys, not whole 64 x 64 tiles. Lanes are
+// laid out as in the split-KV decode kernel: D/8 lanes share a key (8 elements
+// of d each, 16-byte coalesced loads), KPW = 64 / (D/8) keys per load step, U
+// steps per batch; each group of D/8 lanes keeps its own online (m, l, acc),
+// and the groups meet in the (m, l, acc) monoid at the end. Scores are in log2
+// units.
 #include <stdint.h>
 
 #include "launch.h"

@@ -54,10 +54,19 @@ COPY_BYTES = float(1 << 30)
 HASH_SKIP = {"launch.h"}
 
 
+def code_only(text: bytes) -> bytes:
+    """A source with its comments removed and its whitespace collapsed: what the
+    compiler sees of it (a comment edit does not change the kernel)."""
+    text = re.sub(rb"/\*.*?\*/", b" ", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b" ", text)
+    return b" ".join(text.split())
+
+
 def source_sha(name: str, csrc: str = CSRC) -> str:
-    """sha256[:16] over a kernel source and, in include order, every local
-    header it pulls in (``#include "..."``, followed recursively), except the
-    launcher declarations."""
+    """sha256[:16] over the code (comments and whitespace aside) of a kernel
+    source and, in include order, of every local header it pulls in
+    (``#include "..."``, followed recursively), except the launcher
+    declarations."""
     h = hashlib.sha256()
     seen = set(HASH_SKIP)
 
@@ -66,7 +75,7 @@ def source_sha(name: str, csrc: str = CSRC) -> str:
             return
         seen.add(fname)
         text = open(os.path.join(csrc, fname), "rb").read()
-        h.update(text)
+        h.update(code_only(text))
         for inc in re.findall(rb'^#include "([^"]+)"', text, re.M):
             add(inc.decode())
 

@@ -108,3 +108,20 @@ def test_bench_reports_traffic_only_for_the_measured_source(tmp_path, monkeypatc
     assert bench.measured_traffic("decode") is None      # kernel changed since the counters were taken
     assert bench.measured_traffic("prefill") is None     # never measured
     assert bench.measured_traffic("copy") is None        # calibration only
+
+
+def test_source_sha_ignores_comments_but_not_code(tmp_path):
+    """The staleness hash follows the code of a kernel and its local headers:
+    comment and whitespace edits keep it, a code edit or a header's code edit
+    changes it."""
+    from online_softmax_attention_pass_amd import traffic
+    (tmp_path / "h.h").write_text("int f() { return 1; }\n")
+    (tmp_path / "k.hip").write_text('#include "h.h"\n// a kernel\nint g() { return f(); }\n')
+    base = traffic.source_sha("k.hip", str(tmp_path))
+    (tmp_path / "k.hip").write_text('#include "h.h"\n/* another\n comment */\nint g()  {\n return f();  }  // end\n')
+    assert traffic.source_sha("k.hip", str(tmp_path)) == base
+    (tmp_path / "k.hip").write_text('#include "h.h"\nint g() { return f() + 1; }\n')
+    changed = traffic.source_sha("k.hip", str(tmp_path))
+    assert changed != base
+    (tmp_path / "h.h").write_text("int f() { return 2; }\n")
+    assert traffic.source_sha("k.hip", str(tmp_path)) != changed
