@@ -59,10 +59,12 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
     const float* kh = k + bh * int64_t(Lk) * d;
     const float* vh = v + bh * int64_t(Lk) * d;
 
-    __syncthreads();  // previous item's readers of Qs are done
-    for (int i = t; i < kBM * DMAX; i += 256) {
-      const int rr = i / DMAX, e = i % DMAX;
-      Qs[rr][e] = (q0 + rr < Lq && e < d) ? qh[int64_t(q0 + rr) * d + e] : 0.f;
+    // Q of the tile's rows, in registers until the first barrier.
+    float qreg[kBM * DMAX / 256];
+#pragma unroll
+    for (int j = 0; j < kBM * DMAX / 256; ++j) {
+      const int i = t + 256 * j, rr = i / DMAX, e = i % DMAX;
+      qreg[j] = (q0 + rr < Lq && e < d) ? qh[int64_t(q0 + rr) * d + e] : 0.f;
     }
 
     const int qi = q0 + r;  // this lane's query row
@@ -79,27 +81,63 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
 
     // Last key any row of this tile may see under the causal rule.
     const int64_t causal_last = int64_t(min(q0 + kBM, Lq) - 1) + (Lk - Lq);
-    for (int kt = 0; kt < n_kt; ++kt) {
+    // Key tiles this workgroup visits, in order: not past the causal diagonal
+    // of its last row, not wholly before every row's window, not masked out by
+    // the block mask (skipped tiles are never loaded).
+    auto visible = [&](int kt) {
       const int k0 = kt * kBN;
-      if (causal && k0 > causal_last) break;  // every later tile is masked too
-      if (window > 0 && int64_t(k0) + kBN - 1 < lo_first) continue;  // before every row's window
+      if (window > 0 && int64_t(k0) + kBN - 1 < lo_first) return false;
+      const int64_t tile = int64_t(q0 / kMaskTile) * n_mask_cols + k0 / kMaskTile;
+      return block_mask == nullptr || block_mask[tile] != 0;
+    };
+    const int kt_stop = causal ? int(min(int64_t(n_kt), causal_last < 0 ? 0 : causal_last / kBN + 1)) : n_kt;
+    auto next_tile = [&](int kt) {
+      while (kt < kt_stop && !visible(kt)) ++kt;
+      return kt;
+    };
+    // A tile's K, V (this thread's share) and this row's bitmap word, into
+    // registers: the next tile's are issued before the current one is used.
+    constexpr int PER = kBN * DMAX / 256;
+    float kreg[PER], vreg[PER];
+    uint64_t wreg = ~uint64_t(0);
+    auto fetch = [&](int kt) {
+      const int k0 = kt * kBN;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = t + 256 * j, c = i / DMAX, e = i % DMAX;
+        const bool in = (k0 + c < Lk) && e < d;
+        kreg[j] = in ? kh[int64_t(k0 + c) * d + e] : 0.f;
+        vreg[j] = in ? vh[int64_t(k0 + c) * d + e] : 0.f;
+      }
       const int64_t tile = int64_t(q0 / kMaskTile) * n_mask_cols + k0 / kMaskTile;
       const uint8_t kind = block_mask != nullptr ? block_mask[tile] : uint8_t(1);
-      if (kind == 0) continue;  // the whole tile is masked: skip it, no load
       // A partial tile (kind other than 0 and 1, with bitmaps): bit (j mod 64)
       // of this row's word says whether key j is visible. The 16 rows of a
       // workgroup lie in one 64-row mask tile.
-      const bool part = tile_bits != nullptr && kind != 1;
-      uint64_t word = ~uint64_t(0);
-      if (part && qi < Lq) word = tile_bits[tile * kMaskTile + (qi % kMaskTile)];
-      __syncthreads();
-      for (int i = t; i < kBN * DMAX; i += 256) {
-        const int c = i / DMAX, e = i % DMAX;
-        const bool in = (k0 + c < Lk) && e < d;
-        Ks[c][e] = in ? kh[int64_t(k0 + c) * d + e] : 0.f;
-        Vs[c][e] = in ? vh[int64_t(k0 + c) * d + e] : 0.f;
+      wreg = ~uint64_t(0);
+      if (tile_bits != nullptr && kind != 1 && qi < Lq) wreg = tile_bits[tile * kMaskTile + (qi % kMaskTile)];
+    };
+    int kt = next_tile(0);
+    if (kt < kt_stop) fetch(kt);
+    __syncthreads();  // previous item's readers of Qs are done
+#pragma unroll
+    for (int j = 0; j < kBM * DMAX / 256; ++j) {
+      const int i = t + 256 * j;
+      Qs[i / DMAX][i % DMAX] = qreg[j];
+    }
+    while (kt < kt_stop) {
+      const int k0 = kt * kBN;
+      const uint64_t word = wreg;
+      __syncthreads();  // previous tile's readers of Ks, Vs are done
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = t + 256 * j;
+        Ks[i / DMAX][i % DMAX] = kreg[j];
+        Vs[i / DMAX][i % DMAX] = vreg[j];
       }
       __syncthreads();
+      const int kt_next = next_tile(kt + 1);
+      if (kt_next < kt_stop) fetch(kt_next);
 
       // Scores of keys p and p + 16: four partial sums each over 16-byte reads.
       float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -167,6 +205,7 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
           }
         }
       }
+      kt = kt_next;
     }
 
     if (qi < Lq) {
