@@ -42,7 +42,7 @@ hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, vo
                                  const uint8_t* block_mask, const uint64_t* tile_bits, hipStream_t stream,
                                  int window = 0, const float* alibi_slopes = nullptr, float softcap = 0.f);
 // Row-wise masked attention (bf16, d in {64, 128}): one wavefront per query row,
-// only the row's visible key groups. tile_kind NULL = every tile full; tile_bits
+// only the row's visible keys, in batches. tile_kind NULL = every tile full; tile_bits
 // NULL = every nonzero kind is a full tile.
 hipError_t launch_attention_rowwise(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                     int Lq, int Lk, int d, float scale, int causal, const uint8_t* tile_kind,
