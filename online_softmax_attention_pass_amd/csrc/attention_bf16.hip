@@ -302,7 +302,10 @@ __device__ __forceinline__ int64_t work_item(int64_t gi, int64_t n_items, int64_
 //
 // MOD: score modifications (ScoreMod) applied to each score tile before the mask;
 // 1 = bias and window, 2 = also the softcap.
-template <int D, int NW, int WPE, bool BITS, bool SPLIT = false, int MOD = 0>
+//
+// MASK: whether the call has a block mask (or tile kinds); without one the tile
+// walk is a plain count and its state takes no registers.
+template <int D, int NW, int WPE, bool BITS, bool SPLIT = false, int MOD = 0, bool MASK = true>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void attention_bf16_sp_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Lq, int Lk, float c_log2, int q_mode, int causal,
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int64_t lo_first = int64_t(q0) + off - mod.window + 1;
     const int kt_begin = SPLIT ? split * kt_split : ((MOD && mod.window > 0 && lo_first > 0) ? int(lo_first / BN) : 0);
     const int kt_end = SPLIT ? min(kt_all, kt_begin + kt_split) : kt_all;
-    TileWalker walk{block_mask, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+    TileWalker walk{MASK ? block_mask : nullptr, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
                     min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
     walk.bits = BITS;
 
@@ -872,8 +875,8 @@ inline float score_coef(float scale, int* q_mode) {
 
 // One workgroup per item (b, h, query tile); more items than one grid allows go
 // in chunks (then without the XCD placement, which assumes the whole item range).
-template <int D, int NW, int WPE, bool BITS, int MOD = 0>
-hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+template <int D, int NW, int WPE, bool BITS, int MOD = 0, bool MASK = true>
+hipError_t launch_sp_inst(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
                      float scale, int causal, const uint8_t* block_mask, const uint64_t* tile_bits,
                      hipStream_t stream, ScoreMod mod = ScoreMod{}) {
   constexpr int BM = 32 * NW;
@@ -888,7 +891,7 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
       BITS ? uint32_t(int64_t((Lq + kMaskTile - 1) / kMaskTile) * ((Lk + kMaskTile - 1) / kMaskTile) * 512) : 0u;
   for (int64_t base = 0; base < n_items; base += cap) {
     const int64_t n = n_items - base < cap ? n_items - base : cap;
-    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS, false, MOD>), dim3(unsigned(n)), dim3(NW * 64),
+    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS, false, MOD, MASK>), dim3(unsigned(n)), dim3(NW * 64),
                        0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
                        block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base,
@@ -897,6 +900,21 @@ hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// The block-mask-free instance for calls without one (the walk state then
+// costs no registers); element bitmaps always come with tile kinds.
+template <int D, int NW, int WPE, bool BITS, int MOD = 0>
+hipError_t launch_sp(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Lq, int Lk,
+                     float scale, int causal, const uint8_t* block_mask, const uint64_t* tile_bits,
+                     hipStream_t stream, ScoreMod mod = ScoreMod{}) {
+  if constexpr (!BITS) {
+    if (block_mask == nullptr)
+      return launch_sp_inst<D, NW, WPE, BITS, MOD, false>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, nullptr,
+                                                          tile_bits, stream, mod);
+  }
+  return launch_sp_inst<D, NW, WPE, BITS, MOD, true>(q, k, v, o, lse, B, H, Lq, Lk, scale, causal, block_mask,
+                                                     tile_bits, stream, mod);
 }
 
 // Split-KV partials (no mask): items (head, split, query tile), key tiles
@@ -915,7 +933,7 @@ hipError_t launch_split(const void* q, const void* k, const void* v, float* ws_o
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
   for (int64_t base = 0; base < n_items; base += cap) {
     const int64_t n = n_items - base < cap ? n_items - base : cap;
-    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, false, true>), dim3(unsigned(n)), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, false, true, 0, false>), dim3(unsigned(n)), dim3(NW * 64), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), nullptr, nullptr, Lq, Lk, c, q_mode, 0, nullptr, n_qt, n,
                        xcd_remap, 1, base, nullptr, 0u, n_splits, kt_split, ws_o, ws_lse);
