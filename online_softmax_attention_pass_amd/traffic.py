@@ -33,16 +33,16 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNELS = {
     "softmax": ("softmax_rows", "softmax_rows.hip"),
     "layernorm": ("layernorm_rows", "layernorm_rows.hip"),
-    "prefill": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 0>", "attention_bf16.hip"),
-    "sparse": ("attention_bf16_sp_kernel<64, 2, 2, false, false, 0>", "attention_bf16.hip"),
-    "bitmap": ("attention_bf16_sp_kernel<64, 2, 2, true, false, 0>", "attention_bf16.hip"),
+    "prefill": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 0, false>", "attention_bf16.hip"),
+    "sparse": ("attention_bf16_sp_kernel<64, 2, 2, false, false, 0, true>", "attention_bf16.hip"),
+    "bitmap": ("attention_bf16_sp_kernel<64, 2, 2, true, false, 0, true>", "attention_bf16.hip"),
     "decode": ("decode_partial_kernel", "decode_splitkv.hip"),
     "attn_f32": ("attention_f32", "attention_f32.hip"),
-    "gqa": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0>", "attention_bf16.hip"),
-    "mla": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0>", "attention_bf16.hip"),
-    "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
-    "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1>", "attention_bf16.hip"),
-    "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2>", "attention_bf16.hip"),
+    "gqa": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0, false>", "attention_bf16.hip"),
+    "mla": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0, false>", "attention_bf16.hip"),
+    "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),
+    "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),
+    "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2, false>", "attention_bf16.hip"),
     "moe": ("moe_route_kernel", "moe_route.hip"),
     "bigbird": ("attention_rowwise_kernel", "attention_rowwise.hip"),
 }

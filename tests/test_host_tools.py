@@ -37,9 +37,9 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
     names = {
         "softmax": "void rf::softmax_rows_reg<float, 4, 512, 16>(float const*)",
         "layernorm": "void rf::layernorm_rows_reg<float, 4, 512, 16>(float const*)",
-        "prefill": SP.format("128, 4, 2, false, false, 0"),
-        "sparse": SP.format("64, 2, 2, false, false, 0"),
-        "bitmap": SP.format("64, 2, 2, true, false, 0"),
+        "prefill": SP.format("128, 4, 2, false, false, 0, false"),
+        "sparse": SP.format("64, 2, 2, false, false, 0, true"),
+        "bitmap": SP.format("64, 2, 2, true, false, 0, true"),
         "decode": "void rf::decode_partial_kernel<128, 8>(unsigned short const*)",
         "attn_f32": "void rf::attention_f32_kernel<64>(float const*)",
     }
@@ -67,7 +67,7 @@ def test_traffic_keeps_shared_kernels_apart_by_run(tmp_path):
     """Grouped-query and shared-cache decode use one kernel instance, as do the
     ALiBi and window legs: each pair is measured in different runs."""
     copy = "vectorized_elementwise_kernel<MulFunctor>"
-    split, mod1 = SP.format("128, 4, 2, false, true, 0"), SP.format("128, 4, 2, false, false, 1")
+    split, mod1 = SP.format("128, 4, 2, false, true, 0, false"), SP.format("128, 4, 2, false, false, 1, false")
     runs = []
     for r, (wl, kf) in enumerate((("copy,gqa,alibi", 100.0), ("mla,window", 300.0))):
         rows = ([(copy, 524288.0)] if r == 0 else []) + [(split, kf), (mod1, kf + 1)]
