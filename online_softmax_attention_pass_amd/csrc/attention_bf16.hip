@@ -155,6 +155,9 @@ struct ScoreMod {
 // read once per 64 tiles (one byte per lane) and turned into two wave-uniform
 // 64-bit words by ballot: tiles active for any of the workgroup's mask rows, and
 // tiles active for this wave's own mask row. The scan itself is scalar bit work.
+// ONE_ROW: the workgroup's rows are one mask row (64 query rows), so a wave's
+// own words are the workgroup's and are not kept twice.
+template <bool ONE_ROW>
 struct TileWalker {
   const uint8_t* mask;
   int n_mask_cols, mr0, mr1, mr_w, kt_end;
@@ -171,21 +174,21 @@ struct TileWalker {
     bool any = false, mine = false, part = false, anypart = false;
     if (kt < kt_end) {
       const int mc = kt * bn / kMaskTile;
-      for (int mr = mr0; mr <= mr1; ++mr) {
+      for (int mr = mr0; mr <= (ONE_ROW ? mr0 : mr1); ++mr) {
         const uint8_t kind = mask[int64_t(mr) * n_mask_cols + mc];
         const bool a = kind != 0;
         const bool pa = bits && kind != 0 && kind != 1;
         any |= a;
-        mine |= (mr == mr_w) && a;
+        mine |= (ONE_ROW || mr == mr_w) && a;
         anypart |= pa;
-        part |= (mr == mr_w) && pa;
+        part |= (ONE_ROW || mr == mr_w) && pa;
       }
     }
     wg_bits = __builtin_amdgcn_ballot_w64(any);
-    wv_bits = __builtin_amdgcn_ballot_w64(mine);
+    if (!ONE_ROW) wv_bits = __builtin_amdgcn_ballot_w64(mine);
     if (bits) {
       pg_bits = __builtin_amdgcn_ballot_w64(anypart);
-      pv_bits = __builtin_amdgcn_ballot_w64(part);
+      if (!ONE_ROW) pv_bits = __builtin_amdgcn_ballot_w64(part);
     }
     base = b;
   }
@@ -204,8 +207,11 @@ struct TileWalker {
       if (rest) {
         kt += int(__builtin_ctzll(rest));
         if (kt >= kt_end) break;
-        *mine = (wv_bits >> (kt - base)) & 1;
-        if (part != nullptr) *part = int((pv_bits >> (kt - base)) & 1) | (int((pg_bits >> (kt - base)) & 1) << 1);
+        *mine = ONE_ROW ? true : ((wv_bits >> (kt - base)) & 1) != 0;
+        if (part != nullptr) {
+          const int pg = int((pg_bits >> (kt - base)) & 1);
+          *part = ONE_ROW ? pg * 3 : (int((pv_bits >> (kt - base)) & 1) | (pg << 1));
+        }
         return kt;
       }
       kt = base + 64;
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int64_t lo_first = int64_t(q0) + off - mod.window + 1;
     const int kt_begin = SPLIT ? split * kt_split : ((MOD && mod.window > 0 && lo_first > 0) ? int(lo_first / BN) : 0);
     const int kt_end = SPLIT ? min(kt_all, kt_begin + kt_split) : kt_all;
-    TileWalker walk{MASK ? block_mask : nullptr, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+    TileWalker<BM == kMaskTile> walk{MASK ? block_mask : nullptr, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
                     min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
     walk.bits = BITS;
 
