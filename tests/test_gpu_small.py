@@ -325,3 +325,27 @@ def test_output_canaries(rf_gpu):
     torch.cuda.synchronize()
     assert bool((ob[:pad] == 12345).all()) and bool((ob[-pad:] == 12345).all())
     assert bool((lb[:pad] == 7.0).all()) and bool((lb[-pad:] == 7.0).all())
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,Lq,Lk,causal", [(1, 2, 300, 300, True), (2, 1, 200, 333, True), (1, 1, 130, 700, False),
+                                              (1, 3, 64, 64, True), (1, 1, 257, 129, True)])
+def test_attention_bf16_mask_free_equals_all_ones_mask(rf_gpu, d, B, H, Lq, Lk, causal):
+    """A call without a block mask runs the mask-free kernel instance, one with
+    an all-ones mask the masked instance: the same tiles in the same order with
+    the same arithmetic, so the outputs must be identical bit for bit (plain,
+    softcap and window; ALiBi walks the tiles in another order without a mask)."""
+    import torch
+    q, k, v = (dev_bf16(_normal(109, t, (B, H, L, d), "bf16")) for t, L in ((0, Lq), (1, Lk), (2, Lk)))
+    ones = torch.ones((-(-Lq // 64), -(-Lk // 64)), dtype=torch.uint8, device="cuda")
+    note(f"mask-free vs all-ones mask d={d} B={B} H={H} Lq={Lq} Lk={Lk} causal={causal}")
+    for kw in ({}, {"softcap": 30.0}, {"window": 100}):
+        if kw:
+            a = rf_gpu.rf_attention_fwd_mod(q, k, v, causal=causal, **kw)
+            b = rf_gpu.rf_attention_fwd_mod(q, k, v, causal=causal, block_mask=ones, **kw)
+        else:
+            a = rf_gpu.rf_attention_fwd(q, k, v, causal=causal)
+            b = rf_gpu.rf_attention_fwd(q, k, v, causal=causal, block_mask=ones)
+        for x, y, name in zip(a, b, ("O", "LSE")):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), (kw, name)
