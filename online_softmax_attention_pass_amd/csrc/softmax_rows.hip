@@ -72,21 +72,43 @@ __device__ __forceinline__ void block_combine(float& m, float& l, float* sm, flo
 // of EPV elements. Every access goes through row-sized buffer resources: the
 // vectors past the row's end read 0 and are never written, with no branches;
 // the reduction replaces them by -inf.
-template <typename T, int EPV, int BLOCK, int NV>
+// RAGGED (fp32 only): cols need not be a multiple of EPV. The last vector then
+// straddles the row's end: a raw buffer access is range-checked per dword, so
+// its dwords past the end read 0 and are not written, and validity is decided
+// per element. Rows then start only 4-byte aligned, which 16-byte buffer
+// accesses allow.
+template <typename T, int EPV, int BLOCK, int NV, bool RAGGED = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(BLOCK == 1024 && EPV > 1 && NV * EPV == 32 ? 8 : 1))) void softmax_rows_reg(const T* __restrict__ x, T* __restrict__ y,
                                                           int64_t rows, int64_t cols) {
   __shared__ float sm[BLOCK / 64], sl[BLOCK / 64];
   constexpr uint32_t VB = EPV * sizeof(T);  // bytes per vector
-  const int64_t nvec = cols / EPV;          // the host guarantees cols % EPV == 0
+  // vectors touching the row (without RAGGED the host guarantees cols % EPV == 0)
+  const int64_t nvec = RAGGED ? (cols + EPV - 1) / EPV : cols / EPV;
   const uint32_t row_bytes = uint32_t(cols) * uint32_t(sizeof(T));
   const int64_t owned = (nvec - int64_t(threadIdx.x) + BLOCK - 1) / BLOCK;
   const int nv = int(owned < NV ? owned : NV);  // vectors of this lane inside the row
+  // RAGGED: the row's last vector (index nvec - 1) is vector kp of lane lp and
+  // holds rem valid elements (the host keeps ragged rows within 65536 columns).
+  const int kp = RAGGED ? int((nvec - 1) / BLOCK) : 0;
+  const int lp = RAGGED ? int((nvec - 1) % BLOCK) : 0;
+  const int rem = RAGGED ? int(cols - (nvec - 1) * EPV) : EPV;
   for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
     const __amdgpu_buffer_rsrc_t xs = row_rsrc(x + r * cols, row_bytes);
     const __amdgpu_buffer_rsrc_t ys = row_rsrc(y + r * cols, row_bytes);
     float v[NV][EPV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) BufIo<T, EPV>::load(xs, (threadIdx.x + k * BLOCK) * VB, v[k]);
+    if constexpr (RAGGED) {
+      // Only the row's last vector can straddle its end: vector kp of lane lp
+      // (both fixed by cols). Its elements past the end (read as 0) become -inf.
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (k == kp && int(threadIdx.x) == lp) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (e >= rem) v[k][e] = kNegInf;
+        }
+    }
     // Lane-local pair: m_t = max of its elements, l_t = sum_e e^{x_e - m_t}.
     float m = kNegInf;
 #pragma unroll
@@ -165,13 +187,13 @@ __global__ __launch_bounds__(BLOCK) void softmax_rows_stream(const T* __restrict
 // 16k-32k elements goes to 1024 lanes x 32 (64 VGPRs: two workgroups, eight waves
 // per SIMD), which streams faster than 512 lanes x 64 (two workgroups, four waves
 // per SIMD).
-template <typename T, int EPV>
+template <typename T, int EPV, bool RAGGED = false>
 hipError_t dispatch(const T* x, T* y, int64_t rows, int64_t cols, hipStream_t stream) {
-  const int64_t nvec = cols / EPV;
+  const int64_t nvec = RAGGED ? (cols + EPV - 1) / EPV : cols / EPV;
   const unsigned grid = unsigned(rows < (1 << 30) ? rows : (1 << 30));
 #define RF_SOFTMAX_REG(BLOCK, FPL)                                                                  \
   if (nvec <= int64_t(BLOCK) * ((FPL) / EPV)) {                                                    \
-    hipLaunchKernelGGL((softmax_rows_reg<T, EPV, BLOCK, (FPL) / EPV>), dim3(grid), dim3(BLOCK), 0, \
+    hipLaunchKernelGGL((softmax_rows_reg<T, EPV, BLOCK, (FPL) / EPV, RAGGED>), dim3(grid), dim3(BLOCK), 0, \
                        stream, x, y, rows, cols);                                                  \
     return hipGetLastError();                                                                      \
   }
@@ -183,6 +205,7 @@ hipError_t dispatch(const T* x, T* y, int64_t rows, int64_t cols, hipStream_t st
   RF_SOFTMAX_REG(512, 64)
   RF_SOFTMAX_REG(1024, 64)
 #undef RF_SOFTMAX_REG
+  if constexpr (RAGGED) return hipErrorInvalidValue;  // the host keeps ragged rows within the table
   hipLaunchKernelGGL((softmax_rows_stream<T, EPV, 1024>), dim3(grid), dim3(1024), 0, stream, x, y,
                      rows, cols);
   return hipGetLastError();
@@ -197,6 +220,9 @@ hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int64_t col
     const float* xf = static_cast<const float*>(x);
     float* yf = static_cast<float*>(y);
     if (aligned && cols % 4 == 0) return dispatch<float, 4>(xf, yf, rows, cols, stream);
+    // Other widths up to the register table's 65536 columns: 16-byte accesses
+    // all the same, the last vector of a row straddling its end.
+    if (cols <= 65536) return dispatch<float, 4, true>(xf, yf, rows, cols, stream);
     return dispatch<float, 1>(xf, yf, rows, cols, stream);
   }
   const uint16_t* xb = static_cast<const uint16_t*>(x);

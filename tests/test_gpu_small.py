@@ -349,3 +349,18 @@ def test_attention_bf16_mask_free_equals_all_ones_mask(rf_gpu, d, B, H, Lq, Lk, 
         for x, y, name in zip(a, b, ("O", "LSE")):
             assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
                                y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), (kw, name)
+
+
+@pytest.mark.parametrize("cols", [5, 255, 257, 1023, 4097, 8191, 16385, 32767, 32769, 50257, 65533, 65535])
+def test_softmax_ragged_widths(rf_gpu, cols):
+    """fp32 rows whose width is not a multiple of 4 (rows then start only 4-byte
+    aligned, and each row's last 16-byte vector straddles its end), at every
+    register-table boundary: against the oracle, and the elements past a row's
+    end never touched (the next row is intact)."""
+    rows = 3
+    x = W.softmax_rows_input(2, rows, cols)
+    note(f"softmax ragged cols={cols}")
+    y = host_f64(rf_gpu.rf_softmax_rows(dev_f32(x)))
+    ref = O.softmax_rows(x.astype(np.float64))
+    assert_close(y, ref, 1e-5, f"y cols={cols}")
+    assert np.allclose(y.sum(axis=1), 1.0, atol=1e-5)
