@@ -125,7 +125,13 @@ __device__ __forceinline__ void load_affine(__amdgpu_buffer_rsrc_t r, uint32_t o
 // of EPV elements. Every access goes through row-sized buffer resources, so
 // the vectors past the row's end read 0 and are never written, with no
 // branches; only the statistics mask them out.
-template <typename T, int EPV, int BLOCK, int NV>
+//
+// RAGGED (fp32 only): cols need not be a multiple of EPV. The row's last vector
+// then straddles its end (raw buffer accesses are range-checked per dword: the
+// dwords past the end read 0 and are not written); it sits at a slot and lane
+// fixed by cols, and its missing elements are set so that they add nothing to
+// either sum (to x0 before the shift, to the lane mean before the squares).
+template <typename T, int EPV, int BLOCK, int NV, bool RAGGED = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(NV * EPV >= 64 ? 4 : 1))) void layernorm_rows_reg(const T* __restrict__ x, const float* __restrict__ gamma,
                                                             const float* __restrict__ beta, T* __restrict__ y,
                                                             float* __restrict__ mean_out, float* __restrict__ rstd_out,
@@ -133,11 +139,28 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(NV * EPV 
   __shared__ float sn[BLOCK / 64], su[BLOCK / 64], sm2[BLOCK / 64];
   constexpr uint32_t VB = EPV * sizeof(T);      // bytes per row vector
   constexpr uint32_t VA = EPV * sizeof(float);  // bytes per gamma / beta vector
-  const int64_t nvec = cols / EPV;              // the host guarantees cols % EPV == 0
+  // vectors touching the row (without RAGGED the host guarantees cols % EPV == 0)
+  const int64_t nvec = RAGGED ? (cols + EPV - 1) / EPV : cols / EPV;
   const uint32_t row_bytes = uint32_t(cols) * uint32_t(sizeof(T));
   const int64_t owned = (nvec - int64_t(threadIdx.x) + BLOCK - 1) / BLOCK;
   const int nv = int(owned < NV ? owned : NV);  // vectors of this lane inside the row
-  const float n = float(nv * EPV);
+  // RAGGED: the last vector (index nvec - 1) is vector kp of lane lp, rem valid elements.
+  const int kp = RAGGED ? int((nvec - 1) / BLOCK) : 0;
+  const int lp = RAGGED ? int((nvec - 1) % BLOCK) : 0;
+  const int rem = RAGGED ? int(cols - (nvec - 1) * EPV) : EPV;
+  const float n = float(nv * EPV - ((RAGGED && int(threadIdx.x) == lp) ? EPV - rem : 0));
+  // Sets the straddling vector's elements past the row's end to val.
+  auto fill_past_end = [&](float (&v)[NV][EPV], float val) {
+    if constexpr (RAGGED) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k)
+        if (k == kp && int(threadIdx.x) == lp) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e)
+            if (e >= rem) v[k][e] = val;
+        }
+    }
+  };
   const bool has_gamma = gamma != nullptr;
   const __amdgpu_buffer_rsrc_t gs = row_rsrc(gamma, has_gamma ? uint32_t(cols) * 4u : 0u);
   const __amdgpu_buffer_rsrc_t bs = row_rsrc(beta, beta != nullptr ? uint32_t(cols) * 4u : 0u);
@@ -152,6 +175,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(NV * EPV 
     // Lane-local triple, exact two-pass over registers. Vectors past the row's
     // end were read as 0; shifting them by 0 (instead of x0, then u) keeps
     // them 0, so they add nothing to either sum.
+    fill_past_end(v, x0);
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -163,6 +187,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(NV * EPV 
       }
     }
     float u = n > 0.f ? s / n : 0.f;
+    fill_past_end(v, u);
     float m2 = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
@@ -251,10 +276,10 @@ __global__ __launch_bounds__(BLOCK) void layernorm_rows_stream(const T* __restri
   }
 }
 
-template <typename T, int EPV>
+template <typename T, int EPV, bool RAGGED = false>
 hipError_t dispatch(const T* x, const float* gamma, const float* beta, T* y, float* mean, float* rstd, int64_t rows,
                     int64_t cols, float eps, hipStream_t stream) {
-  const int64_t nvec = cols / EPV;
+  const int64_t nvec = RAGGED ? (cols + EPV - 1) / EPV : cols / EPV;
   const unsigned grid = unsigned(rows < (1 << 30) ? rows : (1 << 30));
   // Register variants: up to 64 row elements per lane (32 with single-element
   // access), each within the VGPRs of its occupancy. (1024 lanes x 32 fits 64
@@ -264,7 +289,7 @@ hipError_t dispatch(const T* x, const float* gamma, const float* beta, T* y, flo
 #define RF_LN_REG(BLOCK, FPL)                                                                           \
   if constexpr ((FPL) <= FPL_MAX) {                                                                     \
     if (nvec <= int64_t(BLOCK) * ((FPL) / EPV)) {                                                       \
-      hipLaunchKernelGGL((layernorm_rows_reg<T, EPV, BLOCK, (FPL) / EPV>), dim3(grid), dim3(BLOCK), 0,  \
+      hipLaunchKernelGGL((layernorm_rows_reg<T, EPV, BLOCK, (FPL) / EPV, RAGGED>), dim3(grid), dim3(BLOCK), 0,  \
                          stream, x, gamma, beta, y, mean, rstd, rows, cols, eps);                       \
       return hipGetLastError();                                                                         \
     }                                                                                                   \
@@ -275,6 +300,7 @@ hipError_t dispatch(const T* x, const float* gamma, const float* beta, T* y, flo
   RF_LN_REG(512, 32)
   RF_LN_REG(512, 64)
 #undef RF_LN_REG
+  if constexpr (RAGGED) return hipErrorInvalidValue;  // the host keeps ragged rows within the table
   hipLaunchKernelGGL((layernorm_rows_stream<T, EPV, 1024>), dim3(grid), dim3(1024), 0, stream, x, gamma, beta, y,
                      mean, rstd, rows, cols, eps);
   return hipGetLastError();
@@ -290,6 +316,10 @@ hipError_t launch_layernorm_rows(const void* x, const float* gamma, const float*
     const float* xf = static_cast<const float*>(x);
     float* yf = static_cast<float*>(y);
     if (aligned && cols % 4 == 0) return dispatch<float, 4>(xf, gamma, beta, yf, mean, rstd, rows, cols, eps, stream);
+    // Other widths up to the register table's 32768 columns: 16-byte accesses
+    // all the same, the last vector of a row straddling its end.
+    if (aligned && cols <= 32768)
+      return dispatch<float, 4, true>(xf, gamma, beta, yf, mean, rstd, rows, cols, eps, stream);
     return dispatch<float, 1>(xf, gamma, beta, yf, mean, rstd, rows, cols, eps, stream);
   }
   const uint16_t* xb = static_cast<const uint16_t*>(x);

@@ -74,3 +74,21 @@ def test_layernorm_constant_rows(rf_gpu):
     assert np.array_equal(host_f64(y), np.broadcast_to(b.astype(np.float64), (3, 4096)))
     assert np.allclose(host_f64(rstd), 2.0, rtol=0, atol=1e-6)
     assert np.allclose(host_f64(mean), [7.25, -3.5, 7.25], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("cols", [5, 255, 257, 1023, 4097, 8191, 16385, 32767])
+def test_layernorm_ragged_widths(rf_gpu, cols):
+    """fp32 rows whose width is not a multiple of 4 (16-byte vectors with the
+    last one straddling the row's end; rows start only 4-byte aligned), at
+    every register-table boundary, with gamma and beta: against the oracle."""
+    import torch
+    rows = 3
+    x = W.softmax_rows_input(7, rows, cols)
+    g, b = W.layernorm_affine(7, cols)
+    note(f"layernorm ragged cols={cols}")
+    y, mean, rstd = rf_gpu.rf_layernorm_rows(dev_f32(x), torch.from_numpy(g).cuda(), torch.from_numpy(b).cuda(),
+                                             eps=1e-5)
+    ry, rm, rr = O.layernorm_rows(x.astype(np.float64), g, b, 1e-5)
+    assert_close(host_f64(y), ry, 1e-5, f"y cols={cols}")
+    assert np.all(np.abs(host_f64(mean) - rm) <= 1e-6 * np.abs(rm) + 1e-6)
+    assert np.all(np.abs(host_f64(rstd) - rr) <= 1e-6 * np.abs(rr) + 1e-6)
