@@ -126,7 +126,7 @@ __device__ __forceinline__ void load_affine(__amdgpu_buffer_rsrc_t r, uint32_t o
 // the vectors past the row's end read 0 and are never written, with no
 // branches; only the statistics mask them out.
 //
-// RAGGED (fp32 only): cols need not be a multiple of EPV. The row's last vector
+// RAGGED (fp32, and bf16 of even width): cols need not be a multiple of EPV. The row's last vector
 // then straddles its end (raw buffer accesses are range-checked per dword: the
 // dwords past the end read 0 and are not written); it sits at a slot and lane
 // fixed by cols, and its missing elements are set so that they add nothing to
@@ -325,6 +325,9 @@ hipError_t launch_layernorm_rows(const void* x, const float* gamma, const float*
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* yb = static_cast<uint16_t*>(y);
   if (aligned && cols % 8 == 0) return dispatch<uint16_t, 8>(xb, gamma, beta, yb, mean, rstd, rows, cols, eps, stream);
+  // Even widths: rows start 4-byte aligned and end on a dword boundary.
+  if (aligned && cols % 2 == 0 && cols <= 32768)
+    return dispatch<uint16_t, 8, true>(xb, gamma, beta, yb, mean, rstd, rows, cols, eps, stream);
   return dispatch<uint16_t, 1>(xb, gamma, beta, yb, mean, rstd, rows, cols, eps, stream);
 }
 

@@ -72,11 +72,11 @@ __device__ __forceinline__ void block_combine(float& m, float& l, float* sm, flo
 // of EPV elements. Every access goes through row-sized buffer resources: the
 // vectors past the row's end read 0 and are never written, with no branches;
 // the reduction replaces them by -inf.
-// RAGGED (fp32 only): cols need not be a multiple of EPV. The last vector then
-// straddles the row's end: a raw buffer access is range-checked per dword, so
-// its dwords past the end read 0 and are not written, and validity is decided
-// per element. Rows then start only 4-byte aligned, which 16-byte buffer
-// accesses allow.
+// RAGGED (fp32, and bf16 of even width): cols need not be a multiple of EPV.
+// The last vector then straddles the row's end: a raw buffer access is
+// range-checked per dword, so its dwords past the end read 0 and are not
+// written. Rows start only 4-byte aligned, which 16-byte buffer accesses
+// allow.
 template <typename T, int EPV, int BLOCK, int NV, bool RAGGED = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(BLOCK == 1024 && EPV > 1 && NV * EPV == 32 ? 8 : 1))) void softmax_rows_reg(const T* __restrict__ x, T* __restrict__ y,
                                                           int64_t rows, int64_t cols) {
@@ -228,6 +228,9 @@ hipError_t launch_softmax_rows(const void* x, void* y, int64_t rows, int64_t col
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* yb = static_cast<uint16_t*>(y);
   if (aligned && cols % 8 == 0) return dispatch<uint16_t, 8>(xb, yb, rows, cols, stream);
+  // Even widths: rows start 4-byte aligned and end on a dword boundary, so the
+  // straddling last vector works as for fp32.
+  if (aligned && cols % 2 == 0 && cols <= 65536) return dispatch<uint16_t, 8, true>(xb, yb, rows, cols, stream);
   return dispatch<uint16_t, 1>(xb, yb, rows, cols, stream);
 }
 

@@ -92,3 +92,11 @@ def test_layernorm_ragged_widths(rf_gpu, cols):
     assert_close(host_f64(y), ry, 1e-5, f"y cols={cols}")
     assert np.all(np.abs(host_f64(mean) - rm) <= 1e-6 * np.abs(rm) + 1e-6)
     assert np.all(np.abs(host_f64(rstd) - rr) <= 1e-6 * np.abs(rr) + 1e-6)
+
+
+@pytest.mark.parametrize("cols", [6, 250, 1022, 4094, 16386, 32766])
+def test_layernorm_ragged_even_widths_bf16(rf_gpu, cols):
+    """bf16 rows of even width not a multiple of 8 (16-byte vectors, the last
+    one straddling the row's end on a dword boundary), with gamma and beta."""
+    g, b = W.layernorm_affine(7, cols)
+    _check(rf_gpu, _rows(7, 3, cols), "bf16", g, b, 1e-5, f"ragged bf16 cols={cols}")

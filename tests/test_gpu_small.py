@@ -364,3 +364,16 @@ def test_softmax_ragged_widths(rf_gpu, cols):
     ref = O.softmax_rows(x.astype(np.float64))
     assert_close(y, ref, 1e-5, f"y cols={cols}")
     assert np.allclose(y.sum(axis=1), 1.0, atol=1e-5)
+
+
+@pytest.mark.parametrize("cols", [6, 250, 1022, 4094, 16386, 32766, 50258, 65534])
+def test_softmax_ragged_even_widths_bf16(rf_gpu, cols):
+    """bf16 rows of even width not a multiple of 8: 16-byte vectors, the last
+    one straddling the row's end on a dword boundary; against the oracle on
+    the bf16 inputs (output rounded to bf16)."""
+    rows = 3
+    x = W.f32_to_bf16_bits(W.softmax_rows_input(2, rows, cols))
+    note(f"softmax bf16 ragged cols={cols}")
+    y = host_f64(rf_gpu.rf_softmax_rows(dev_bf16(x)))
+    ref = O.softmax_rows(O.bf16_bits_to_f64(x))
+    assert_close(y, ref, 1e-2, f"y cols={cols}")
