@@ -110,6 +110,23 @@ class Timer:
         return mean_ms, per, wall
 
 
+WARM_MS = 25.0  # the least warm-up time, whatever the call count
+
+
+def warm_up(torch, fn, calls):
+    """At least `calls` untimed calls, and more until WARM_MS of them have run:
+    after the input set-up the GPU has idled, and on this chip the first few
+    milliseconds of steady calls run slower while the clock settles."""
+    n, t0 = 0, time.perf_counter()
+    while n < calls or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        fn()
+        n += 1
+        if n >= calls and n % 8 == 0:
+            torch.cuda.synchronize()   # pace the host to the GPU so elapsed time is GPU time
+    torch.cuda.synchronize()
+    return n
+
+
 def roofline(bound, achieved, peak, unit, traffic):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -447,16 +464,13 @@ def main():
     for name in wanted:
         log(f"{name}: setup")
         s = SETUPS[name](rf, torch, W)
-        for _ in range(args.warmup):
-            s["fn"]()
-        torch.cuda.synchronize()
-        log(f"{name}: timing {args.steps} calls")
+        n_warm = warm_up(torch, s["fn"], args.warmup)
+        log(f"{name}: timing {args.steps} calls (after {n_warm} warm-up calls)")
         call_ms, per, wall = timer.run(s["fn"], args.steps)
         kern_ms = call_ms
         merge_ms = None
         if "subtract" in s:
-            for _ in range(args.warmup):
-                s["subtract"]()
+            warm_up(torch, s["subtract"], args.warmup)
             merge_ms, _, _ = timer.run(s["subtract"], args.steps)
             kern_ms = call_ms - merge_ms
         thr = s["work"] / (call_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
@@ -465,13 +479,13 @@ def main():
         r = {"workload": s["cfg"]["name"], "value": round(thr, 3), "unit": s["unit"],
              "ms_per_call": round(call_ms, 5), "ms_p10": round(float(np.percentile(per, 10)), 5),
              "ms_p90": round(float(np.percentile(per, 90)), 5), "wall_s": round(wall, 4),
-             "roofline": roofline(s["bound"], kthr, peak, s["unit"], measured_traffic(name))}
+             "roofline": roofline(s["bound"], kthr, peak, s["unit"], measured_traffic(name)),
+             "warmup_calls": n_warm}
         if merge_ms is not None:
             r["merge_ms"] = round(merge_ms, 5)
             r["partial_kernel_ms"] = round(kern_ms, 5)
         for alt, fn in s.get("alternatives", {}).items():
-            for _ in range(args.warmup):
-                fn()
+            warm_up(torch, fn, args.warmup)
             r[f"{alt}_ms"] = round(timer.run(fn, args.steps)[0], 5)
         if "flops" in s:
             r["tflops"] = round(s["flops"] / (call_ms * 1e-3) / 1e12, 3)
