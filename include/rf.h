@@ -217,7 +217,7 @@ int rf_attention_fwd_mod(const void* q, const void* k, const void* v, void* o, f
  *               tile full); tile_bits : uint64 [same tiles, 64] or NULL (every
  *               nonzero kind is a full tile), 8-byte aligned.
  *   q, k, v, o, lse and scale as rf_attention_fwd; q, k, v, o 16-byte aligned.
- * Supported: RF_BF16 with d in {64, 128}.
+ * Supported: RF_BF16 with d in {64, 128} and Lk * d * 2 < 2^31 bytes per head.
  * Errors: RF_ERR_INVALID_ARG, RF_ERR_UNSUPPORTED, RF_ERR_HIP.
  */
 int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* o, float* lse,

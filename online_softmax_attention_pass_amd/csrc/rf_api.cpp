@@ -164,6 +164,8 @@ int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* 
       return fail(RF_ERR_INVALID_ARG, "%s: tile_bits must be 8-byte aligned", name);
     if (tile_bits != nullptr && Lk > 0 && tile_kind == nullptr)
       return fail(RF_ERR_INVALID_ARG, "%s: NULL tile_kind", name);
+    if (int64_t(Lk) * d * 2 > INT32_MAX)
+      return fail(RF_ERR_UNSUPPORTED, "%s: needs Lk * d * 2 < 2^31 bytes per head", name);
     return hip_status(rf::launch_attention_rowwise(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal != 0, tile_kind,
                                                    tile_bits, static_cast<hipStream_t>(stream)),
                       name);
@@ -174,11 +176,6 @@ int rf_attention_fwd_rowwise(const void* q, const void* k, const void* v, void* 
   }
 }
 
-// Cost model of the two masked kernels on MI355X, in microseconds per call
-// (fitted to measured calls of both kernels over masks of many densities):
-//   tile kernel: a launch term, plus a term per 64 x 64 tile of MFMA work,
-//   row kernel : a launch term, plus a term per query row, plus a term per key
-//                group the rows visit.
 namespace {
 // Cost of one masked call on MI355X, in microseconds: a launch term plus the
 // larger of a throughput term (all the work spread over the chip) and a

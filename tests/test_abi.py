@@ -396,7 +396,7 @@ def att_row(lib, **kw):
     (dict(dtype=9), INVALID), (dict(B=-1), INVALID), (dict(d=0), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(dtype=F32), UNSUP), (dict(d=96), UNSUP), (dict(q=NUL), INVALID), (dict(k=NUL), INVALID),
     (dict(o=P(0x10008)), UNSUP), (dict(bits=FAKE), INVALID), (dict(bits=P(0x10004), kinds=FAKE), INVALID),
-    (dict(B=0), OK), (dict(Lq=0), OK),
+    (dict(B=0), OK), (dict(Lq=0), OK), (dict(Lk=1 << 23), UNSUP),   # 2^23 keys x 128 x 2 B = 2^31 per head
 ])
 def test_rowwise_validation(lib, kw, code):
     assert att_row(lib, **kw) == code
