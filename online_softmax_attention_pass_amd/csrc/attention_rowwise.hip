@@ -76,16 +76,47 @@ __global__ __launch_bounds__(256) void attention_rowwise_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
-    // The row's visible keys in order, gathered into batches of KB keys. The
-    // mask is read 64 tiles at a time: lane j reads tile J0 + j's kind and this
-    // row's word of it, and a ballot keeps the tiles with a visible key. Each
-    // such tile's word comes back to the whole wave by readlane, and its set
-    // bits are appended, in order, to this wave's list of pending keys in LDS
-    // (a 64-entry ring): lane j writes key k0 + j at its rank among the set bits.
+    // The row's visible keys, gathered into batches of KB keys (in a fixed
+    // order: per chunk of 64 tiles, the sparse tiles' keys, then the dense
+    // tiles'). The mask is read 64 tiles at a time: lane j reads tile J0 + j's
+    // kind and this row's word of it. A dense tile's word comes back to the
+    // whole wave by readlane, and its set bits are appended to this wave's list
+    // of pending keys in LDS (a 64-entry ring): lane j writes key k0 + j at its
+    // rank among the set bits.
+    // Tiles with at most kSparse visible keys (most of a sparse row) are not
+    // visited one by one: every lane holding such a tile writes its keys at
+    // once, at positions from a wave-wide exclusive scan of the counts (three
+    // ballots of the count's bits and mbcnt), as long as the ring has room.
+    // Denser tiles go one at a time, all lanes writing one key each.
+    constexpr int kSparse = 4;
     int J0 = -kRowTile, k0 = 0, head = 0, n_pend = 0;
-    uint64_t wl = 0, todo = 0, word = 0;
+    uint64_t wl = 0, todo = 0, word = 0, ws = 0;  // ws: this lane's sparse tile keys still to take
+    bool sparse_left = false;
+    auto mbcnt64 = [](uint64_t m) {
+      return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+    };
     auto fill = [&]() {
       while (n_pend < KB) {
+        if (sparse_left) {
+          const int cnt = __builtin_popcountll(ws);  // 0 .. kSparse
+          const uint64_t b0 = __builtin_amdgcn_ballot_w64((cnt & 1) != 0);
+          const uint64_t b1 = __builtin_amdgcn_ballot_w64((cnt & 2) != 0);
+          const uint64_t b2 = __builtin_amdgcn_ballot_w64((cnt & 4) != 0);
+          const int excl = mbcnt64(b0) + 2 * mbcnt64(b1) + 4 * mbcnt64(b2);
+          const int total = __builtin_popcountll(b0) + 2 * __builtin_popcountll(b1) + 4 * __builtin_popcountll(b2);
+          const int room = 64 - n_pend;
+          uint64_t w = ws;
+#pragma unroll
+          for (int j = 0; j < kSparse; ++j)
+            if (w != 0 && excl + j < room) {
+              pend[(head + n_pend + excl + j) & 63] = (J0 + lane) * kRowTile + __builtin_ctzll(w);
+              w &= w - 1;
+            }
+          ws = w;
+          n_pend += total < room ? total : room;
+          sparse_left = __builtin_amdgcn_ballot_w64(ws != 0) != 0;
+          continue;
+        }
         if (word == 0) {
           if (todo == 0) {
             J0 += 64;
@@ -102,7 +133,10 @@ __global__ __launch_bounds__(256) void attention_rowwise_kernel(
                 wl &= (uint64_t(1) << n) - 1;
               }
             }
-            todo = __builtin_amdgcn_ballot_w64(wl != 0);
+            const bool dense = __builtin_popcountll(wl) > kSparse;
+            ws = dense ? 0 : wl;
+            todo = __builtin_amdgcn_ballot_w64(dense);
+            sparse_left = __builtin_amdgcn_ballot_w64(ws != 0) != 0;
             continue;
           }
           const int jl = __builtin_ctzll(todo);
@@ -112,8 +146,8 @@ __global__ __launch_bounds__(256) void attention_rowwise_kernel(
           word = (uint64_t(hi) << 32) | lo;
           k0 = (J0 + jl) * kRowTile;
         }
-        // Take as many of the tile's keys as the ring has room for.
-        const int rank = int(__builtin_amdgcn_mbcnt_hi(uint32_t(word >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(word), 0u)));
+        // Take as many of the dense tile's keys as the ring has room for.
+        const int rank = mbcnt64(word);
         const bool take = ((word >> lane) & 1) != 0 && rank < 64 - n_pend;
         if (take) pend[(head + n_pend + rank) & 63] = k0 + lane;
         const uint64_t taken = __builtin_amdgcn_ballot_w64(take);

@@ -192,8 +192,8 @@ struct PlanCost {
   double row_per_tile;                                  // batches per visited tile
 };
 PlanCost plan_cost(int d) {
-  if (d == 128) return {12.0, 3.94e-3, 0.96, 12.0, 6.08e-4, 5e-4, 0.25};
-  return {10.0, 2.65e-3, 1.50, 12.0, 8.35e-4, 0.854, 0.1};
+  if (d == 128) return {11.0, 3.36e-3, 1.05, 12.0, 7.12e-4, 5e-4, 0.1};
+  return {10.0, 2.65e-3, 1.50, 13.0, 7.12e-4, 5e-4, 0.1};
 }
 }  // namespace
 
