@@ -3,10 +3,11 @@
 // page, Metodologia 3). Used for fp32 inputs with any head dim d <= 128.
 //
 // A workgroup of 256 lanes owns BM = 16 query rows of one (b, h) and sweeps
-// the visible key tiles of BN = 32 keys. Lane (r, p) = (t / 16, t % 16) holds
-// query row r: it scores keys p and p + 16 of the tile and accumulates the
-// output columns [p * DMAX / 16, (p + 1) * DMAX / 16) of row r, so the running
-// (m, l) of a row lives in the 16 lanes that share it. Masked key tiles are
+// the visible key tiles of BN keys (64 for d <= 64, else 32). Lane
+// (r, p) = (t / 16, t % 16) holds query row r: it scores keys p, p + 16, ...
+// of the tile and accumulates the output columns
+// [p * DMAX / 16, (p + 1) * DMAX / 16) of row r, so the running (m, l) of a
+// row lives in the 16 lanes that share it. Masked key tiles are
 // skipped before any load (STOF page, Énoncé du problème / Méthodologie 1:
 // skip rather than compute and reset); only tiles that straddle the causal
 // diagonal or the end of the keys are masked per element.
@@ -24,7 +25,7 @@
 namespace rf {
 namespace {
 
-constexpr int kBM = 16, kBN = 32, kMaskTile = 64;
+constexpr int kBM = 16, kMaskTile = 64;
 
 template <int DMAX>
 __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
@@ -39,7 +40,12 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
   // instruction reads start 4 banks apart.
   constexpr int DP = DMAX + 4;
   constexpr int NC = DMAX / 16;  // output columns per lane
+  // Keys per step: 64 (one mask tile) while the tile's K and V fit the
+  // register double buffer, so a short sequence takes half the dependent steps.
+  constexpr int kBN = DMAX <= 64 ? 64 : 32;
+  constexpr int NK = kBN / 16;  // keys scored per lane and step
   static_assert(DMAX % 16 == 0, "column split");
+  static_assert(kMaskTile % kBN == 0, "a key tile lies in one mask tile");
   __shared__ __align__(16) float Qs[kBM][DP];
   __shared__ __align__(16) float Ks[kBN][DP];
   __shared__ __align__(16) float Vs[kBN][DP];
@@ -139,34 +145,33 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
       const int kt_next = next_tile(kt + 1);
       if (kt_next < kt_stop) fetch(kt_next);
 
-      // Scores of keys p and p + 16: four partial sums each over 16-byte reads.
-      float pa[4] = {0.f, 0.f, 0.f, 0.f}, pb[4] = {0.f, 0.f, 0.f, 0.f};
+      // Scores of keys p + 16 j: four partial sums each over 16-byte reads.
+      float pk[NK][4];
+#pragma unroll
+      for (int j = 0; j < NK; ++j) pk[j][0] = pk[j][1] = pk[j][2] = pk[j][3] = 0.f;
 #pragma unroll
       for (int e = 0; e < DMAX; e += 4) {
         const float4 qv = *reinterpret_cast<const float4*>(&Qs[r][e]);
-        const float4 ka = *reinterpret_cast<const float4*>(&Ks[p][e]);
-        const float4 kb = *reinterpret_cast<const float4*>(&Ks[p + 16][e]);
-        pa[0] = fmaf(qv.x, ka.x, pa[0]);
-        pa[1] = fmaf(qv.y, ka.y, pa[1]);
-        pa[2] = fmaf(qv.z, ka.z, pa[2]);
-        pa[3] = fmaf(qv.w, ka.w, pa[3]);
-        pb[0] = fmaf(qv.x, kb.x, pb[0]);
-        pb[1] = fmaf(qv.y, kb.y, pb[1]);
-        pb[2] = fmaf(qv.z, kb.z, pb[2]);
-        pb[3] = fmaf(qv.w, kb.w, pb[3]);
+#pragma unroll
+        for (int j = 0; j < NK; ++j) {
+          const float4 kv = *reinterpret_cast<const float4*>(&Ks[p + 16 * j][e]);
+          pk[j][0] = fmaf(qv.x, kv.x, pk[j][0]);
+          pk[j][1] = fmaf(qv.y, kv.y, pk[j][1]);
+          pk[j][2] = fmaf(qv.z, kv.z, pk[j][2]);
+          pk[j][3] = fmaf(qv.w, kv.w, pk[j][3]);
+        }
       }
-      float s[2];
-      const float dots[2] = {(pa[0] + pa[1]) + (pa[2] + pa[3]), (pb[0] + pb[1]) + (pb[2] + pb[3])};
+      float s[NK];
       float bm = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NK; ++j) {
         const int kj = k0 + p + 16 * j;
         const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= int64_t(qi) + (Lk - Lq)) &&
                          ((word >> (kj % kMaskTile)) & 1) && int64_t(kj) >= lo;
         // s = scale (q . k) in log2 units; the softcap cap tanh(s / cap) moves
         // to log2 units as (cap log2 e) tanh(t / (cap log2 e)); ALiBi adds
         // slope (j - p_i).
-        float t2 = dots[j] * scale_log2;
+        float t2 = ((pk[j][0] + pk[j][1]) + (pk[j][2] + pk[j][3])) * scale_log2;
         if (softcap > 0.f) t2 = softcap * kLog2e * tanhf(t2 / (softcap * kLog2e));
         t2 = fmaf(sl2, float(int64_t(kj) - qpos), t2);
         s[j] = vis ? t2 : kNegInf;
@@ -176,10 +181,14 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
       const float mn = fmaxf(m, bm);
       const float mu = (mn == kNegInf) ? 0.f : mn;
       const float alpha = fast_exp2(m - mu);
-      const float p0 = fast_exp2(s[0] - mu), p1 = fast_exp2(s[1] - mu);
-      Ps[r][p] = p0;
-      Ps[r][p + 16] = p1;
-      l = l * alpha + group_sum<16>(p0 + p1);
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const float pj = fast_exp2(s[j] - mu);
+        Ps[r][p + 16 * j] = pj;
+        psum += pj;
+      }
+      l = l * alpha + group_sum<16>(psum);
       m = mn;
       __syncthreads();
 #pragma unroll
