@@ -13,7 +13,7 @@ active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds).
 Extension workloads: element bitmaps in partial tiles (B2 H16 L8192 d64,
 TFLOP/s), row layer normalisation (fp32 4096 x 32768, GB/s), and decode with
 grouped queries at Lk 32768, d 128: 8 query heads per key/value head (B64 Hq64
-Hkv8, 4 splits) and 128 query heads on one cache (B64 Hq128 Hkv1, 16 splits),
+Hkv8, 4 splits) and 128 query heads on one cache (B64 Hq128 Hkv1, 8 splits),
 in GB/s with TFLOP/s alongside; and the score modifications on the causal
 prefill shape (B4 H32 L4096 d128): ALiBi bias, tanh softcap 50, and a
 1024-key sliding window (TFLOP/s); and mixture-of-experts routing of 131072

@@ -210,9 +210,9 @@ EXTENSION_CONFIGS = {
     # k and v as [B, Hkv, Lk, d], per head like every other tensor.
     "gqa_decode": dict(name="gqa_decode_bf16_B64_Hq64_Hkv8_Lk32768_d128_s4", kind="decode_gqa", dtype="bf16",
                        B=64, Hq=64, Hkv=8, Lk=32768, d=128, scale=1.0 / math.sqrt(128), num_splits=4, seed=8),
-    "mla_decode": dict(name="shared_kv_decode_bf16_B64_Hq128_Hkv1_Lk32768_d128_s16", kind="decode_gqa",
+    "mla_decode": dict(name="shared_kv_decode_bf16_B64_Hq128_Hkv1_Lk32768_d128_s8", kind="decode_gqa",
                        dtype="bf16", B=64, Hq=128, Hkv=1, Lk=32768, d=128, scale=1.0 / math.sqrt(128),
-                       num_splits=16, seed=9),
+                       num_splits=8, seed=9),
     # Score modifications (the FlexAttention variants) on the causal prefill
     # shape: one set of q, k, v for three variants, each on top of causal: an
     # ALiBi bias with the geometric slopes, a tanh softcap of 50, and an
