@@ -48,6 +48,9 @@ namespace {
 
 // Launch shape per head dim: waves per workgroup (32 query rows each) and
 // waves per SIMD the register allocation must allow.
+#ifndef RF_SPLIT_SMALL_TILES
+#define RF_SPLIT_SMALL_TILES 1
+#endif
 #ifndef RF_ATT_NW_D128
 #define RF_ATT_NW_D128 4
 #endif
@@ -954,9 +957,21 @@ hipError_t launch_split(const void* q, const void* k, const void* v, float* ws_o
 hipError_t launch_attention_bf16_split(const void* q, const void* k, const void* v, float* ws_o, float* ws_lse,
                                        int n_heads, int Lq, int Lk, int d, float scale, int n_splits,
                                        hipStream_t stream) {
-  if (d == 128)
+  // A decode item has as many query rows as query heads share a key/value
+  // head. Where they fill only a fraction of the 128-row tile, a 32- or
+  // 64-row workgroup does the same K/V streaming with a quarter or a half of
+  // the padded matrix and softmax work, which otherwise competes with the
+  // stream for issue slots.
+  if (d == 128) {
+#if RF_SPLIT_SMALL_TILES
+    if (Lq <= 32)
+      return launch_split<128, 1, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
+    if (Lq <= 64)
+      return launch_split<128, 2, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
+#endif
     return launch_split<128, RF_ATT_NW_D128, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale,
                                                                n_splits, stream);
+  }
   return launch_split<64, RF_ATT_NW_D64, RF_ATT_WPE_D64>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits,
                                                           stream);
 }

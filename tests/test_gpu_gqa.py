@@ -48,6 +48,10 @@ GQA_CASES = [  # B, Hq, Hkv, Lk, d, S
     (1, 4, 4, 1, 128, 2),          # one key
     (1, 12, 4, 64, 64, 1),         # exactly one tile, written directly
     (2, 24, 3, 2049, 128, 1),      # G = 8, no split
+    (1, 32, 1, 1500, 128, 3),      # G = 32: one full 32-row tile
+    (1, 66, 2, 1100, 128, 4),      # G = 33: a 64-row tile, ragged
+    (1, 64, 1, 900, 128, 2),       # G = 64: one full 64-row tile
+    (1, 65, 1, 700, 128, 3),       # G = 65: a 128-row tile
 ]
 
 

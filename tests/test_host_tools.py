@@ -64,14 +64,17 @@ def test_traffic_scales_by_the_copy_calibration(tmp_path):
 
 
 def test_traffic_keeps_shared_kernels_apart_by_run(tmp_path):
-    """Grouped-query and shared-cache decode use one kernel instance, as do the
-    ALiBi and window legs: each pair is measured in different runs."""
+    """The ALiBi and window legs use one kernel instance: they are measured in
+    different runs, and a run that holds both is rejected. Grouped-query
+    decode (8 query heads per key/value head, 32-row tiles) and shared-cache
+    decode (128-row tiles) use different instances."""
     copy = "vectorized_elementwise_kernel<MulFunctor>"
-    split, mod1 = SP.format("128, 4, 2, false, true, 0, false"), SP.format("128, 4, 2, false, false, 1, false")
+    gqa_k, split = SP.format("128, 1, 2, false, true, 0, false"), SP.format("128, 4, 2, false, true, 0, false")
+    mod1 = SP.format("128, 4, 2, false, false, 1, false")
     runs = []
-    for r, (wl, kf) in enumerate((("copy,gqa,alibi", 100.0), ("mla,window", 300.0))):
-        rows = ([(copy, 524288.0)] if r == 0 else []) + [(split, kf), (mod1, kf + 1)]
-        wrows = ([(copy, 1048576.0)] if r == 0 else []) + [(split, kf), (mod1, kf + 1)]
+    for r, (wl, kn, kf) in enumerate((("copy,gqa,alibi", gqa_k, 100.0), ("mla,window", split, 300.0))):
+        rows = ([(copy, 524288.0)] if r == 0 else []) + [(kn, kf), (mod1, kf + 1)]
+        wrows = ([(copy, 1048576.0)] if r == 0 else []) + [(kn, kf), (mod1, kf + 1)]
         f, w = tmp_path / f"f{r}.csv", tmp_path / f"w{r}.csv"
         _write_counters(f, "FETCH_SIZE", rows)
         _write_counters(w, "WRITE_SIZE", wrows)
@@ -82,7 +85,7 @@ def test_traffic_keeps_shared_kernels_apart_by_run(tmp_path):
     assert t["gqa"]["fetch_bytes"] == 100 * 2048 and t["alibi"]["fetch_bytes"] == 101 * 2048
     assert t["mla"]["fetch_bytes"] == 300 * 2048 and t["window"]["write_bytes"] == 301 * 1024
     with pytest.raises(SystemExit):                    # one run may not hold both users of a kernel
-        traffic.main([str(out), runs[0].replace("copy,gqa,alibi", "copy,gqa,mla")])
+        traffic.main([str(out), runs[0].replace("copy,gqa,alibi", "copy,gqa,alibi,window")])
 
 
 def test_traffic_rejects_an_ambiguous_kernel(tmp_path):
