@@ -139,8 +139,8 @@ def roofline(bound, achieved, peak, unit, traffic):
 def setup_softmax(rf, torch, W):
     """Two input/output sets (2 GiB), used alternately, so that no call finds
     its operands in the 256 MB Infinity Cache left by the previous one."""
-    c = W.CONFIGS[2]
-    x = W.softmax_rows_input(2, c["rows"], c["cols"])
+    c = W.CONFIGS["softmax"]
+    x = W.softmax_rows_input(c["seed"], c["rows"], c["cols"])
     sets = []
     for _ in range(2):
         xd = torch.from_numpy(x).cuda()
@@ -157,8 +157,8 @@ def setup_softmax(rf, torch, W):
 
 
 def setup_prefill(rf, torch, W):
-    c = W.CONFIGS[3]
-    q, k, v = (torch.from_numpy(W.normal_tensor(3, t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
+    c = W.CONFIGS["prefill"]
+    q, k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
                .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
     o = torch.empty_like(q)
     lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
@@ -199,10 +199,10 @@ def setup_window(rf, torch, W):
 
 
 def setup_sparse(rf, torch, W):
-    c = W.CONFIGS[5]
-    q, k, v = (torch.from_numpy(W.normal_tensor(5, t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
+    c = W.CONFIGS["sparse"]
+    q, k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
                .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
-    bm = W.config_block_mask(5)
+    bm = W.config_block_mask("sparse")
     bmd = torch.from_numpy(bm).cuda()
     o = torch.empty_like(q)
     lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
@@ -301,11 +301,11 @@ def setup_bigbird(rf, torch, W):
 
 
 def setup_decode(rf, torch, W):
-    c = W.CONFIGS[4]
+    c = W.CONFIGS["decode"]
     B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
 
     def up(t, L):
-        a = W.normal_tensor(4, t, B, H, L, d, "bf16")
+        a = W.normal_tensor(c["seed"], t, B, H, L, d, "bf16")
         x = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         del a
         return x
@@ -381,8 +381,8 @@ def setup_moe(rf, torch, W):
 
 
 def setup_attn_f32(rf, torch, W):
-    c = W.CONFIGS[1]
-    q, k, v = (torch.from_numpy(W.normal_tensor(1, t, 1, 1, 128, 64, "f32")).cuda()
+    c = W.CONFIGS["attn_f32"]
+    q, k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, 1, 1, 128, 64, "f32")).cuda()
                for t in (W.TID_Q, W.TID_K, W.TID_V))
     o = torch.empty_like(q)
     lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
@@ -414,14 +414,14 @@ def cpu_baseline_softmax(W, budget_s=10.0):
     """The fp64 oracle over the headline workload's rows, 64 rows at a time,
     repeating whole passes until about budget_s of oracle time is spent."""
     import oracle
-    c = W.CONFIGS[2]
+    c = W.CONFIGS["softmax"]
     chunk = 64
     rows = 0
     spent = 0.0
     cpu = 0.0
     while spent < budget_s:
         r0 = rows % c["rows"]
-        x = W.softmax_rows_input(2, chunk, c["cols"], row_ids=range(r0, r0 + chunk))
+        x = W.softmax_rows_input(c["seed"], chunk, c["cols"], row_ids=range(r0, r0 + chunk))
         t0, p0 = time.perf_counter(), time.process_time()
         oracle.softmax_rows(x)
         spent += time.perf_counter() - t0

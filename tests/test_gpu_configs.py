@@ -34,34 +34,34 @@ def _same_again(first, again, what):
 
 def _qkv_full(cfg):
     c = W.CONFIGS[cfg]
-    return [W.normal_tensor(cfg, tid, c["B"], c["H"], L, c["d"], c["dtype"])
+    return [W.normal_tensor(c["seed"], tid, c["B"], c["H"], L, c["d"], c["dtype"])
             for tid, L in ((W.TID_Q, c.get("Lq", 1)), (W.TID_K, c["Lk"]), (W.TID_V, c["Lk"]))]
 
 
-def test_config1_attention_f32(rf_gpu):
-    c = W.CONFIGS[1]
-    q, k, v = _qkv_full(1)
-    note("config 1 full")
+def test_single_head_attention_f32(rf_gpu):
+    c = W.CONFIGS["attn_f32"]
+    q, k, v = _qkv_full("attn_f32")
+    note("single-head fp32 attention, full")
     o, lse = rf_gpu.rf_attention_fwd(dev_f32(q), dev_f32(k), dev_f32(v), scale=c["scale"], causal=False)
     ref_o, ref_lse = O.attention(q, k, v, c["scale"])
-    e_o = assert_close(host_f64(o), ref_o, 1e-5, "config 1 O")
-    e_l = assert_close(host_f64(lse), ref_lse, 1e-3, "config 1 LSE")
-    _report("config1", e_o, e_l)
+    e_o = assert_close(host_f64(o), ref_o, 1e-5, "attn_f32 O")
+    e_l = assert_close(host_f64(lse), ref_lse, 1e-3, "attn_f32 LSE")
+    _report("attn_f32", e_o, e_l)
 
 
 def test_config2_softmax_rows(rf_gpu):
     import torch
-    c = W.CONFIGS[2]
-    x = W.softmax_rows_input(2, c["rows"], c["cols"])
-    note("config 2 full")
+    c = W.CONFIGS["softmax"]
+    x = W.softmax_rows_input(c["seed"], c["rows"], c["cols"])
+    note("softmax rows, full")
     y = rf_gpu.rf_softmax_rows(dev_f32(x))
     sums = y.double().sum(dim=1)
     assert float((sums - 1).abs().max()) < 1e-4                  # every row sums to 1
     assert bool(torch.isfinite(y).all()) and float(y.min()) >= 0
     rows = sorted({0, 1, 63, 64, 2047, 2048, 4094, 4095, *W.rng(2, 99).choice(4096, 56, replace=False).tolist()})
     got = host_f64(y[rows])
-    e = assert_close(got, O.softmax_rows(x[rows]), 1e-5, "config 2 y")
-    _report("config2 (64 sampled rows)", e, 0.0)
+    e = assert_close(got, O.softmax_rows(x[rows]), 1e-5, "softmax y")
+    _report("softmax (64 sampled rows)", e, 0.0)
 
 
 def _sample_rows(L, seed):
@@ -71,21 +71,21 @@ def _sample_rows(L, seed):
     return sorted(r for r in edge | set(rand) if 0 <= r < L)
 
 
-@pytest.mark.parametrize("cfg", [3, 5])
+@pytest.mark.parametrize("cfg", ["prefill", "sparse"])
 def test_config_attention_bf16(rf_gpu, cfg):
     import torch
     c = W.CONFIGS[cfg]
     q, k, v = _qkv_full(cfg)
     bm = W.config_block_mask(cfg)
-    note(f"config {cfg} full")
+    note(f"{cfg} full")
     qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
     bmd = None if bm is None else torch.from_numpy(bm).cuda()
     o, lse = rf_gpu.rf_attention_fwd(qd, kd, vd, scale=c["scale"], causal=c["causal"], block_mask=bmd)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
     _same_again((o, lse), rf_gpu.rf_attention_fwd(qd, kd, vd, scale=c["scale"], causal=c["causal"], block_mask=bmd),
-                f"config {cfg}")
+                f"{cfg}")
     heads = [(0, 0), (c["B"] - 1, c["H"] - 1), (c["B"] // 2, c["H"] // 3), (0, c["H"] - 2)]
-    rows = _sample_rows(c["Lq"], cfg)
+    rows = _sample_rows(c["Lq"], c["seed"])
     worst_o = worst_l = 0.0
     refs = []
     for b, h in heads:
@@ -97,33 +97,33 @@ def test_config_attention_bf16(rf_gpu, cfg):
         worst_o = max(worst_o, max_abs_err(got_o, ref_o[0, 0]))
         worst_l = max(worst_l, max_abs_err(got_l, ref_lse[0, 0]))
         refs.append(ref_o[0, 0])
-    _report(f"config{cfg} ({len(heads)} heads x {len(rows)} rows)", worst_o, worst_l, np.concatenate(refs))
+    _report(f"{cfg} ({len(heads)} heads x {len(rows)} rows)", worst_o, worst_l, np.concatenate(refs))
     assert worst_o <= 1e-2 and worst_l <= 1e-3
 
 
 def test_config4_decode(rf_gpu):
     import torch
-    c = W.CONFIGS[4]
+    c = W.CONFIGS["decode"]
     B, H, Lk, d, S = c["B"], c["H"], c["Lk"], c["d"], c["num_splits"]
-    q = W.normal_tensor(4, W.TID_Q, B, H, 1, d, "bf16")
-    note("config 4: generating K/V (32 GiB)")
-    k = W.normal_tensor(4, W.TID_K, B, H, Lk, d, "bf16")
+    q = W.normal_tensor(c["seed"], W.TID_Q, B, H, 1, d, "bf16")
+    note("split-KV decode: generating K/V (32 GiB)")
+    k = W.normal_tensor(c["seed"], W.TID_K, B, H, Lk, d, "bf16")
     kd = dev_bf16(k)
     del k
-    v = W.normal_tensor(4, W.TID_V, B, H, Lk, d, "bf16")
+    v = W.normal_tensor(c["seed"], W.TID_V, B, H, Lk, d, "bf16")
     vd = dev_bf16(v)
     del v
-    note("config 4 full")
+    note("split-KV decode, full")
     qd = dev_bf16(q)
     o, lse = rf_gpu.rf_attention_decode_splitkv(qd, kd, vd, scale=c["scale"], num_splits=S)
     assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
-    _same_again((o, lse), rf_gpu.rf_attention_decode_splitkv(qd, kd, vd, scale=c["scale"], num_splits=S), "config 4")
+    _same_again((o, lse), rf_gpu.rf_attention_decode_splitkv(qd, kd, vd, scale=c["scale"], num_splits=S), "split-KV decode")
     heads = [(0, 0), (B - 1, H - 1), (17, 5), (40, 30), (63, 0), (5, 16)]
     worst_o = worst_l = 0.0
     refs = []
     for b, h in heads:
-        kh = W.normal_head(4, W.TID_K, b, h, Lk, d, "bf16")[None, None]
-        vh = W.normal_head(4, W.TID_V, b, h, Lk, d, "bf16")[None, None]
+        kh = W.normal_head(c["seed"], W.TID_K, b, h, Lk, d, "bf16")[None, None]
+        vh = W.normal_head(c["seed"], W.TID_V, b, h, Lk, d, "bf16")[None, None]
         ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(q[b:b + 1, h:h + 1]), O.bf16_bits_to_f64(kh),
                                      O.bf16_bits_to_f64(vh), c["scale"])
         worst_o = max(worst_o, max_abs_err(host_f64(o[b, h]), ref_o[0, 0]))

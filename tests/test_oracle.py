@@ -395,7 +395,7 @@ def test_workload_generators_are_pure_functions_of_the_seed():
 
 
 def test_config5_mask_counts():
-    m = W.config_block_mask(5)
+    m = W.config_block_mask("sparse")
     assert m.shape == (128, 128)
     window = sum(min(i + 1, 8) for i in range(128))
     assert window == 996

@@ -34,18 +34,18 @@ MASK_TILE = 64  # granularity of the block mask, in tokens, on both axes
 
 # The five workloads. Sizes are the ones the throughput figures are quoted on.
 CONFIGS = {
-    1: dict(name="attn_f32_B1_H1_L128_d64", kind="attention", dtype="f32",
+    "attn_f32": dict(seed=1, name="attn_f32_B1_H1_L128_d64", kind="attention", dtype="f32",
             B=1, H=1, Lq=128, Lk=128, d=64, scale=1.0 / math.sqrt(64),
             causal=False, mask=None),
-    2: dict(name="softmax_f32_4096x32768", kind="softmax", dtype="f32",
+    "softmax": dict(seed=2, name="softmax_f32_4096x32768", kind="softmax", dtype="f32",
             rows=4096, cols=32768),
-    3: dict(name="causal_prefill_bf16_B4_H32_L4096_d128", kind="attention",
+    "prefill": dict(seed=3, name="causal_prefill_bf16_B4_H32_L4096_d128", kind="attention",
             dtype="bf16", B=4, H=32, Lq=4096, Lk=4096, d=128,
             scale=1.0 / math.sqrt(128), causal=True, mask=None),
-    4: dict(name="splitkv_decode_bf16_B64_H32_Lk32768_d128_s16",
+    "decode": dict(seed=4, name="splitkv_decode_bf16_B64_H32_Lk32768_d128_s16",
             kind="decode", dtype="bf16", B=64, H=32, Lk=32768, d=128,
             scale=1.0 / math.sqrt(128), num_splits=16),
-    5: dict(name="block_sparse_bf16_B2_H16_L8192_d64", kind="attention",
+    "sparse": dict(seed=5, name="block_sparse_bf16_B2_H16_L8192_d64", kind="attention",
             dtype="bf16", B=2, H=16, Lq=8192, Lk=8192, d=64,
             scale=1.0 / math.sqrt(64), causal=True, mask="window512_rand10"),
 }
@@ -275,12 +275,12 @@ def extension_bitmap_mask():
     return window_bitmap_mask(c["seed"], c["Lq"], window=512, frac=0.10)
 
 
-def config_block_mask(cfg: int):
-    c = CONFIGS[cfg]
+def config_block_mask(name: str):
+    c = CONFIGS[name]
     if c.get("mask") != "window512_rand10":
         return None
     n = math.ceil(c["Lq"] / MASK_TILE)
-    return window_random_block_mask(cfg, n, window_tiles=512 // MASK_TILE, frac=0.10)
+    return window_random_block_mask(c["seed"], n, window_tiles=512 // MASK_TILE, frac=0.10)
 
 
 def element_mask_tiles(vis: np.ndarray):
