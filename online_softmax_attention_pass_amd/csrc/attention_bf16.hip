@@ -60,6 +60,9 @@ namespace {
 #ifndef RF_ATT_NW_D64
 #define RF_ATT_NW_D64 2
 #endif
+#ifndef RF_ATT_PRIO
+#define RF_ATT_PRIO 1
+#endif
 #ifndef RF_ATT_SREAD_AHEAD
 #define RF_ATT_SREAD_AHEAD 4
 #endif
@@ -646,6 +649,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       l_rnd += ltr;
     };
     static_assert(MB == 2, "two halves per tile");
+    // Wave priority: at d = 128 a wave issuing its score MFMAs (phase A) or
+    // the pure MFMA run of phase B2 wins the SIMD's arbitration over the other
+    // wave's softmax work, so the matrix core is fed first and that vector work
+    // fills the cycles between MFMAs (about 2% on causal prefill). At d = 64,
+    // where the vector work per MFMA doubles, it measured no better.
+    constexpr bool kIssuePrio = RF_ATT_PRIO != 0 && D >= 128;
     // Steady-state step with the exponentials split across both phases:
     //   phase A : S(next) MFMAs     with the exponentials of keys 0..31
     //   phase B1: P.V keys 0..31    with the exponentials of keys 32..63
@@ -670,6 +679,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         };
         const float mu = (m_ref == kNegInf) ? 0.f : m_ref;
         uint4 kfrag[KAHEAD];
+        if constexpr (kIssuePrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < KAHEAD; ++i) kfrag[i] = kread(i);
 #pragma unroll
@@ -684,6 +694,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           __builtin_amdgcn_sched_barrier(0);
 #endif
         }
+        if constexpr (kIssuePrio) __builtin_amdgcn_s_setprio(0);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pk[0][i]));
@@ -726,7 +737,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         });
         mask_tile(s_next, kt_next, mine_next, part_next, ~uint64_t(0));
       } else {
+        if constexpr (kIssuePrio) __builtin_amdgcn_s_setprio(1);
         pv_range(vs_cur, pk, NPV / 2, NPV, [](int) {});
+        if constexpr (kIssuePrio) __builtin_amdgcn_s_setprio(0);
       }
     };
     // The last tile: exponentials and P.V product only.
