@@ -63,6 +63,9 @@ namespace {
 #ifndef RF_ATT_PRIO
 #define RF_ATT_PRIO 1
 #endif
+#ifndef RF_ATT_SREAD_AHEAD_D128
+#define RF_ATT_SREAD_AHEAD_D128 2
+#endif
 #ifndef RF_ATT_SREAD_AHEAD
 #define RF_ATT_SREAD_AHEAD 4
 #endif
@@ -339,6 +342,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   constexpr int IPW = INSTR / NW;
   static_assert(INSTR % NW == 0, "tile split");
   using SW = Swz<D>;
+  // K fragments read ahead of the score MFMAs: two at d = 128 measured 0.8%
+  // faster on causal prefill than four (with the wave priority below).
+  constexpr int kSreadAhead = D >= 128 ? RF_ATT_SREAD_AHEAD_D128 : RF_ATT_SREAD_AHEAD;
+  static_assert(kSreadAhead > 0, "read-ahead");
 
   __shared__ __align__(16) uint16_t kb0[BN * D];
   __shared__ __align__(16) uint16_t kb1[BN * D];
@@ -442,7 +449,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[a][r] = 0.f;
       // K fragments in a rolling window of KAHEAD reads ahead of their product.
-      constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
+      constexpr int KAHEAD = kSreadAhead;
       auto kread = [&](int i) {
         const int kstep = i / MB, mb = i % MB;
         const int row = 32 * mb + l32;
@@ -671,7 +678,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         for (int a = 0; a < MB; ++a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_next[a][r] = 0.f;
-        constexpr int KAHEAD = RF_ATT_SREAD_AHEAD > 0 ? RF_ATT_SREAD_AHEAD : 1;
+        constexpr int KAHEAD = kSreadAhead;
         auto kread = [&](int i) {
           const int kstep = i / MB, mb = i % MB;
           const int row = 32 * mb + l32;
