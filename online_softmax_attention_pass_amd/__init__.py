@@ -122,6 +122,19 @@ def _ptr(t):
         else ctypes.c_void_p(0)
 
 
+def _check_out(o, shape, dtype, what="out"):
+    """A caller-supplied output must have the exact shape and dtype the kernel writes:
+    the C ABI sees only a pointer, so a smaller or narrower tensor would be overrun."""
+    if tuple(o.shape) != tuple(shape) or o.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype} {tuple(shape)}, got {o.dtype} {tuple(o.shape)}")
+
+
+def _check_same_dtype(q, *ts):
+    for t in ts:
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v must share a dtype")
+
+
 def rf_abi_version() -> int:
     return load().rf_abi_version()
 
@@ -231,6 +244,8 @@ def rf_attention_fwd_mod(q, k, v, scale=None, causal=False, block_mask=None, win
         raise ValueError("out must match q")
     if lse is None and want_lse:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, H, Lq), torch.float32, "lse")
     dev = _dev(q, k, v, o, lse, block_mask, alibi_slopes)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -297,12 +312,16 @@ def rf_attention_decode_splitkv(q, k, v, scale=None, num_splits=16, workspace=No
     Lk = k.shape[2]
     if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
         raise ValueError("k, v must be [B, H, Lk, d] matching q")
+    _check_same_dtype(q, k, v)
     ws_bytes = rf_attention_decode_splitkv_workspace_size(B, H, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q.shape, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, H), torch.float32, "lse")
     dev = _dev(q, k, v, o, lse, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -329,12 +348,16 @@ def rf_attention_decode_gqa(q, k, v, scale=None, num_splits=1, workspace=None, o
     Hkv, Lk = k.shape[1], k.shape[2]
     if k.shape != (B, Hkv, Lk, d) or v.shape != (B, Hkv, Lk, d):
         raise ValueError("k, v must be [B, Hkv, Lk, d] matching q")
+    _check_same_dtype(q, k, v)
     ws_bytes = rf_attention_decode_gqa_workspace_size(B, Hq, d, num_splits)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q.shape, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, Hq), torch.float32, "lse")
     dev = _dev(q, k, v, o, lse, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -355,10 +378,13 @@ def rf_lse_merge(o_parts, lse_parts, out_dtype=None, out=None, lse=None, want_ls
         raise ValueError("lse_parts must be [n, S]")
     if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
         raise ValueError("partials must be fp32")
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    out_dtype = (torch.float32 if out is None else out.dtype) if out_dtype is None else out_dtype
     o = torch.empty((n, d), dtype=out_dtype, device=o_parts.device) if out is None else out
+    _check_out(o, (n, d), out_dtype)
     if lse is None and want_lse:
         lse = torch.empty((n,), dtype=torch.float32, device=o_parts.device)
+    if lse is not None:
+        _check_out(lse, (n,), torch.float32, "lse")
     dev = _dev(o_parts, lse_parts, o, lse)
     st = lib.rf_lse_merge(_ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse), n, S, d, _dtype_code(o),
                           _stream(dev))
@@ -402,9 +428,13 @@ def rf_attention_fwd_rowwise(q, k, v, tile_kind=None, tile_bits=None, scale=None
         raise ValueError(f"tile_kind must be uint8 {(nI, nJ)}")
     if tile_bits is not None and (tile_bits.element_size() != 8 or tuple(tile_bits.shape) != (nI, nJ, MASK_TILE)):
         raise ValueError(f"tile_bits must be 64-bit {(nI, nJ, MASK_TILE)}")
+    _check_same_dtype(q, k, v)
     o = torch.empty_like(q) if out is None else out
+    _check_out(o, q.shape, q.dtype)
     if lse is None and want_lse:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, H, Lq), torch.float32, "lse")
     dev = _dev(q, k, v, o, lse, tile_kind, tile_bits)
     if scale is None:
         scale = 1.0 / math.sqrt(d)

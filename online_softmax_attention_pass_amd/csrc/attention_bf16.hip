@@ -849,15 +849,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           }
         if (h == 0) ws_lse[prow] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
       }
-      return;
-    }
+    } else {
     // Output: each wave's 32 rows are one contiguous block of O. Lanes l and
     // l + 32 hold alternate 8-byte pieces of a row; one v_permlane32_swap per
     // dword gives each lane a 16-byte run, which goes through this wave's own
     // slice of the (now idle) K buffers so that every store instruction writes
     // 1 KiB of consecutive bytes.
     {
-      static_assert(NW * 32 <= 2 * BN, "output staging fits in the K buffers");
+      static_assert(NW >= 2 && NW * 32 <= 2 * BN, "output staging: a wave pair per K buffer");
       constexpr int OCH = D / 8;  // 16-byte chunks per row
       uint16_t* stage = (wave < NW / 2 ? kb0 : kb1) + (wave % (NW / 2)) * 32 * D;
 #pragma unroll
@@ -884,6 +883,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       }
     }
     if (lse != nullptr && h == 0 && qi < Lq) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 

@@ -402,3 +402,87 @@ def test_rowwise_validation(lib, kw, code):
     assert att_row(lib, **kw) == code
     if code != OK:
         assert "rf_attention_fwd_rowwise" in _msg(lib)
+
+
+# ---------------------------------------------------------------------------
+# Binding checks on caller-supplied outputs: the C ABI sees only pointers, so
+# the binding must refuse an output of the wrong shape or dtype before the
+# call (CPU tensors: the checks run before the device check).
+# ---------------------------------------------------------------------------
+
+def _t(*shape, dtype="bf16"):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("case", ["o_shape", "o_dtype", "lse_shape", "lse_dtype", "kv_dtype"])
+def test_binding_decode_splitkv_checks_outputs(case):
+    q, k, v = _t(2, 3, 1, 64), _t(2, 3, 100, 64), _t(2, 3, 100, 64)
+    kw = {}
+    if case == "o_shape":
+        kw["out"] = _t(2, 3, 1, 32)
+    elif case == "o_dtype":
+        kw["out"] = _t(2, 3, 1, 64, dtype="f32")
+    elif case == "lse_shape":
+        kw["lse"] = _t(2, 2, dtype="f32")
+    elif case == "lse_dtype":
+        kw["lse"] = _t(2, 3)
+    else:
+        k = _t(2, 3, 100, 64, dtype="f32")
+    with pytest.raises(ValueError):
+        rf.rf_attention_decode_splitkv(q, k, v, num_splits=4, **kw)
+
+
+@pytest.mark.parametrize("case", ["o_shape", "o_dtype", "lse_shape", "kv_dtype"])
+def test_binding_decode_gqa_checks_outputs(case):
+    q, k, v = _t(2, 8, 64), _t(2, 2, 100, 64), _t(2, 2, 100, 64)
+    kw = {}
+    if case == "o_shape":
+        kw["out"] = _t(2, 4, 64)
+    elif case == "o_dtype":
+        kw["out"] = _t(2, 8, 64, dtype="f32")
+    elif case == "lse_shape":
+        kw["lse"] = _t(2, 2, dtype="f32")
+    else:
+        v = _t(2, 2, 100, 64, dtype="f32")
+    with pytest.raises(ValueError):
+        rf.rf_attention_decode_gqa(q, k, v, num_splits=2, **kw)
+
+
+@pytest.mark.parametrize("case", ["o_shape", "o_dtype", "lse_shape", "lse_dtype"])
+def test_binding_lse_merge_checks_outputs(case):
+    op, lp = _t(5, 3, 64, dtype="f32"), _t(5, 3, dtype="f32")
+    kw = {}
+    if case == "o_shape":
+        kw["out"] = _t(4, 64, dtype="f32")
+    elif case == "o_dtype":
+        kw.update(out=_t(5, 64, dtype="f32"), out_dtype=_t(1).dtype)
+    elif case == "lse_shape":
+        kw["lse"] = _t(3, dtype="f32")
+    else:
+        kw["lse"] = _t(5)
+    with pytest.raises(ValueError):
+        rf.rf_lse_merge(op, lp, **kw)
+
+
+def test_binding_attention_mod_checks_lse():
+    q = _t(1, 2, 70, 64)
+    with pytest.raises(ValueError):
+        rf.rf_attention_fwd_mod(q, q, q, window=16, lse=_t(1, 2, 69, dtype="f32"))
+    with pytest.raises(ValueError):
+        rf.rf_attention_fwd_mod(q, q, q, window=16, lse=_t(1, 2, 70))
+
+
+@pytest.mark.parametrize("case", ["o_shape", "lse_shape", "kv_dtype"])
+def test_binding_rowwise_checks_outputs(case):
+    q = _t(1, 2, 70, 64)
+    k = _t(1, 2, 70, 64)
+    kw = {}
+    if case == "o_shape":
+        kw["out"] = _t(1, 2, 70, 32)
+    elif case == "lse_shape":
+        kw["lse"] = _t(1, 2, 71, dtype="f32")
+    else:
+        k = _t(1, 2, 70, 64, dtype="f32")
+    with pytest.raises(ValueError):
+        rf.rf_attention_fwd_rowwise(q, k, k, **kw)
