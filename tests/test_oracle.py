@@ -1152,3 +1152,87 @@ def test_moe_route_mutants_are_caught(kind):
         assert not (pin_moe_bruteforce(fn) and pin_moe_closed_forms(fn) and pin_moe_invariances(fn))
     none = _moe_mutant("none")
     assert pin_moe_bruteforce(none) and pin_moe_closed_forms(none) and pin_moe_invariances(none)
+
+
+# ---------------------------------------------------------------------------
+# The oracle's process pool (full-output parity and the CPU baseline) splits
+# work by head and by block of rows only: its results equal the serial
+# oracle's exactly.
+# ---------------------------------------------------------------------------
+
+def test_pool_attention_row_blocks_equal_serial():
+    from oracle import pool
+    import workloads as W
+    c = W.CONFIGS["attn_f32"]
+    blocks = [(0, 50), (50, 51), (51, 128)]
+    got = pool.map_tasks("attention", [("attn_f32", 0, 0, r0, r1) for r0, r1 in blocks], workers=3)
+    q, k, v = (W.normal_tensor(c["seed"], t, 1, 1, 128, 64, "f32") for t in (W.TID_Q, W.TID_K, W.TID_V))
+    ro, rl = O.attention(q, k, v, c["scale"])
+    # the BLAS may block a 50-row and a 128-row product differently: the
+    # summation order of a dot product, and only that, may change
+    assert np.abs(np.concatenate([g[0] for g in got]) - ro[0, 0]).max() <= 1e-14
+    assert np.abs(np.concatenate([g[1] for g in got]) - rl[0, 0]).max() <= 1e-14
+
+
+def test_pool_masked_bf16_head_rows_equal_serial():
+    from oracle import pool
+    import workloads as W
+    c = W.CONFIGS["sparse"]
+    rows = (4000, 4100)
+    (go, gl), = pool.map_tasks("attention", [("sparse", 1, 7, *rows)], workers=1)
+    q, k, v = (O.bf16_bits_to_f64(W.normal_head(c["seed"], t, 1, 7, c["Lq"], c["d"], "bf16"))[None, None]
+               for t in (W.TID_Q, W.TID_K, W.TID_V))
+    ro, rl = O.attention(q, k, v, c["scale"], True, W.config_block_mask("sparse"), q_rows=np.arange(*rows))
+    assert np.array_equal(go, ro[0, 0]) and np.array_equal(gl, rl[0, 0])   # same rows, same calls
+
+
+def test_pool_softmax_and_decode_equal_serial():
+    from oracle import pool
+    import workloads as W
+    got = pool.map_tasks("softmax", [("softmax", 0, 3), ("softmax", 4090, 4096)], workers=2)
+    c = W.CONFIGS["softmax"]
+    want = O.softmax_rows(W.softmax_rows_input(c["seed"], 6, c["cols"], row_ids=[0, 1, 2, 4093, 4094, 4095][:3]))
+    assert np.array_equal(got[0], want)
+    assert got[1].shape == (6, c["cols"])
+    c = W.CONFIGS["decode"]
+    (go, gl), = pool.map_tasks("decode", [("decode", 65, 67)], workers=1)
+    for i, bh in enumerate((65, 66)):
+        b, h = divmod(bh, c["H"])
+        q, k, v = (O.bf16_bits_to_f64(W.normal_head(c["seed"], t, b, h, L, c["d"], "bf16"))[None, None]
+                   for t, L in ((W.TID_Q, 1), (W.TID_K, c["Lk"]), (W.TID_V, c["Lk"])))
+        ro, rl = O.attention(q, k, v, c["scale"])
+        assert np.array_equal(go[i], ro[0, 0, 0]) and gl[i] == rl[0, 0, 0]
+
+
+def test_pool_timed_run_reports_workers():
+    from oracle import pool
+    r = pool.timed_run("attention", [("attn_f32", 0, 0, 0, 64), ("attn_f32", 0, 0, 64, 128)], workers=2)
+    assert r["workers"] == 2 and r["tasks"] == 2 and r["wall_s"] > 0
+
+
+# ---------------------------------------------------------------------------
+# The full-output bf16 gate: planted mistakes in a copy of an oracle result
+# ---------------------------------------------------------------------------
+
+def test_bf16_gate_accepts_rounded_and_flags_planted_errors():
+    import full_oracle as F
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((2, 3, 50, 8))
+    ref[0, 1, 7, 5] = -4.139159435727643          # its nearest bf16 is 0.01416 away: gate unattainable
+    lse = rng.standard_normal((2, 3, 50))
+    lse[1, 2, 0] = -np.inf
+    good = O.round_to_bf16(ref)
+    r = F.check_bf16_gates("t", good, lse.copy(), ref, lse)
+    assert r["max_err_o"] > 1e-2 and r["max_err_o_gated"] <= 2.0 ** -7 and len(r["unattainable"]) == 1
+    other = good.copy()
+    other[0, 1, 7, 5] = -4.15625                   # the other bf16 neighbour: still accepted
+    F.check_bf16_gates("t", other, lse, ref, lse)
+    for mutate in (lambda o, l: o.__setitem__((1, 0, 3, 2), o[1, 0, 3, 2] + 0.011),     # one element off
+                   lambda o, l: o.__setitem__((0, 1, 7, 5), -4.1875),                   # two spacings off
+                   lambda o, l: l.__setitem__((0, 0, 4), l[0, 0, 4] + 2e-3),            # LSE off
+                   lambda o, l: l.__setitem__((1, 2, 0), 0.0),                          # -inf lost
+                   lambda o, l: o.__setitem__((0, 0, 0, 0), np.nan)):
+        o2, l2 = good.copy(), lse.copy()
+        mutate(o2, l2)
+        with pytest.raises(AssertionError):
+            F.check_bf16_gates("t", o2, l2, ref, lse)

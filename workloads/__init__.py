@@ -236,13 +236,23 @@ EXTENSION_CONFIGS = {
 TID_LOGITS = 8
 
 
+MOE_DRAW_BLOCK = 4096   # tokens per generator: block t0 .. t0 + 4095 comes from rng(seed, TID_LOGITS, t0)
+
+
+def moe_logits_block(seed: int, t0: int, t1: int, E: int) -> np.ndarray:
+    """Tokens [t0, t1) of the router logits (t0 a multiple of MOE_DRAW_BLOCK)."""
+    assert t0 % MOE_DRAW_BLOCK == 0
+    x = np.empty((t1 - t0, E), np.float32)
+    for b in range(t0, t1, MOE_DRAW_BLOCK):
+        n = min(t1, b + MOE_DRAW_BLOCK) - b
+        x[b - t0:b - t0 + n] = 2.0 * rng(seed, TID_LOGITS, b).standard_normal((n, E), dtype=np.float32)
+    return x
+
+
 def moe_logits(seed: int, T: int, E: int, quantum: float = 0.0) -> np.ndarray:
-    """Router logits [T, E] float32 ~ N(0, 2^2), drawn per token; quantum > 0
-    rounds them to multiples of it (many exact ties)."""
-    x = np.empty((T, E), np.float32)
-    for t0 in range(0, T, 4096):
-        t1 = min(T, t0 + 4096)
-        x[t0:t1] = 2.0 * rng(seed, TID_LOGITS, t0).standard_normal((t1 - t0, E), dtype=np.float32)
+    """Router logits [T, E] float32 ~ N(0, 2^2), drawn in blocks of 4096 tokens;
+    quantum > 0 rounds them to multiples of it (many exact ties)."""
+    x = moe_logits_block(seed, 0, T, E)
     if quantum > 0:
         x = (np.round(x / quantum) * quantum).astype(np.float32)
     return x
