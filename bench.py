@@ -19,14 +19,24 @@ prefill shape (B4 H32 L4096 d128): ALiBi bias, tanh softcap 50, and a
 1024-key sliding window (TFLOP/s); and mixture-of-experts routing of 131072
 tokens over 256 experts, top 8 (GB/s).
 
-Timing: inputs are resident in HBM before the timed region; W untimed
-warm-up calls; then K calls, each bracketed by HIP events recorded on the
-stream the kernels run on; the whole region is bracketed by device syncs.
-The softmax workload (HBM-bound, 1 GiB per call) alternates two buffer sets
-so that no call is served from the 256 MB Infinity Cache; decode's 32 GiB
-cannot be cached; the MFMA-bound attention workloads use one set.
-The CPU baseline times the fp64 oracle on a bounded sample of the headline
-workload, on this host's cores, and scales it to the same unit.
+Timing: every leg's inputs are made resident in HBM first; then, once,
+about 100 ms of untimed calls of the first leg (the GPU has idled while the
+host drew the inputs, and its clock needs that long to settle; reported as
+``settle``); then leg after leg, back to back: exactly W untimed warm-up
+calls, then K calls between one pair of HIP events recorded on the stream the
+kernels run on (the mean per call), then K more, each bracketed by its own
+events (the spread); device syncs bracket each region. No call finds its
+operands in the 256 MB Infinity Cache left by earlier calls: the softmax and
+layer-norm workloads (1 GiB per call) alternate two buffer sets, the
+block-sparse and bitmap workloads (about 135 MB) rotate three, the MoE and
+BigBird workloads two; the prefill-shape workloads (512 MiB of q, k, v, o),
+the decodes (1 to 32 GiB) exceed the cache by themselves.
+The split-KV and grouped-query decodes' roofline is over the whole call (the
+partial kernel plus the merge); the partial kernel alone is reported beside
+it, labelled.
+CPU baseline: after the GPU legs, the fp64 oracle as it stands, on a bounded
+sample of each workload, over all of this host's cores (one forked process
+per core, at most 16, BLAS one thread each), in each leg's own unit.
 """
 from __future__ import annotations
 
@@ -110,18 +120,27 @@ class Timer:
         return mean_ms, per, wall
 
 
-WARM_MS = 25.0  # the least warm-up time, whatever the call count
+SETTLE_MS = 100.0  # untimed GPU work before the first leg
 
 
 def warm_up(torch, fn, calls):
-    """At least `calls` untimed calls, and more until WARM_MS of them have run:
-    after the input set-up the GPU has idled, and on this chip the first few
-    milliseconds of steady calls run slower while the clock settles."""
+    """Exactly `calls` untimed calls."""
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize()
+    return calls
+
+
+def settle(torch, fn, ms):
+    """Untimed calls for `ms` milliseconds, once, before the first leg: the GPU
+    has idled while the host drew the inputs, and on this chip the first
+    milliseconds of steady calls after an idle period run slower while the
+    clock settles."""
     n, t0 = 0, time.perf_counter()
-    while n < calls or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+    while (time.perf_counter() - t0) * 1e3 < ms:
         fn()
         n += 1
-        if n >= calls and n % 8 == 0:
+        if n % 8 == 0:
             torch.cuda.synchronize()   # pace the host to the GPU so elapsed time is GPU time
     torch.cuda.synchronize()
     return n
@@ -198,19 +217,42 @@ def setup_window(rf, torch, W):
     return _setup_score_mod(rf, torch, W, "window")
 
 
+N_SETS_SMALL = 3   # buffer sets for workloads whose operands (~135 MB) would fit the 256 MB Infinity Cache
+
+
+def _rotating_sets(torch, make, n):
+    """n independent copies of a workload's device buffers, used in turn, so
+    that no call finds its operands in the 256 MB Infinity Cache left by the
+    previous calls (n x the working set > 256 MB)."""
+    sets = [make() for _ in range(n)]
+    state = {"i": 0}
+
+    def next_set():
+        x = sets[state["i"] % n]
+        state["i"] += 1
+        return x
+    return sets, next_set
+
+
 def setup_sparse(rf, torch, W):
     c = W.CONFIGS["sparse"]
     q, k, v = (torch.from_numpy(W.normal_tensor(c["seed"], t, c["B"], c["H"], c["Lq"], c["d"], "bf16").view(np.int16))
                .view(torch.bfloat16).cuda() for t in (W.TID_Q, W.TID_K, W.TID_V))
     bm = W.config_block_mask("sparse")
     bmd = torch.from_numpy(bm).cuda()
-    o = torch.empty_like(q)
-    lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
+    lse_shape = (c["B"], c["H"], c["Lq"])
+    sets, next_set = _rotating_sets(torch, lambda: (q.clone(), k.clone(), v.clone(), torch.empty_like(q),
+                                                    torch.empty(lse_shape, dtype=torch.float32, device="cuda")),
+                                    N_SETS_SMALL)
+    del q, k, v
     flops = 4 * 64 * 64 * c["d"] * int(bm.sum()) * c["B"] * c["H"]   # active 64x64 tiles, counted whole
-    return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], causal=True, block_mask=bmd, out=o,
-                                               lse=lse),
-                work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, bmd, o, lse), cfg=c,
-                extra={"active_tiles_per_head": int(bm.sum()), "tiles_per_head": int(bm.size)})
+
+    def fn():
+        q, k, v, o, lse = next_set()
+        rf.rf_attention_fwd(q, k, v, scale=c["scale"], causal=True, block_mask=bmd, out=o, lse=lse)
+    return dict(fn=fn, work=flops, unit="TFLOP/s", bound="mfma", keep=(sets, bmd), cfg=c,
+                extra={"active_tiles_per_head": int(bm.sum()), "tiles_per_head": int(bm.size),
+                       "buffer_sets": N_SETS_SMALL})
 
 
 def setup_layernorm(rf, torch, W):
@@ -246,18 +288,24 @@ def setup_bitmap(rf, torch, W):
     kinds, bits = W.extension_bitmap_mask()
     kd = torch.from_numpy(kinds).cuda()
     bd = torch.from_numpy(bits.view(np.int64)).cuda()
-    o = torch.empty_like(q)
-    lse = torch.empty((c["B"], c["H"], c["Lq"]), dtype=torch.float32, device="cuda")
+    lse_shape = (c["B"], c["H"], c["Lq"])
+    sets, next_set = _rotating_sets(torch, lambda: (q.clone(), k.clone(), v.clone(), torch.empty_like(q),
+                                                    torch.empty(lse_shape, dtype=torch.float32, device="cuda")),
+                                    N_SETS_SMALL)
+    del q, k, v
     active = int((kinds != 0).sum())
     flops = 4 * 64 * 64 * c["d"] * active * c["B"] * c["H"]   # active 64x64 tiles, counted whole
     n_full = int((kinds == 1).sum())
     n_vis_part = int(sum(bin(int(w)).count("1") for w in bits[kinds == 2].ravel()))
     visible = n_full * 64 * 64 + n_vis_part
-    return dict(fn=lambda: rf.rf_attention_fwd_bitmap(q, k, v, kd, bd, scale=c["scale"], causal=c["causal"], out=o,
-                                                      lse=lse),
-                work=flops, unit="TFLOP/s", bound="mfma", keep=(q, k, v, kd, bd, o, lse), cfg=c,
+
+    def fn():
+        q, k, v, o, lse = next_set()
+        rf.rf_attention_fwd_bitmap(q, k, v, kd, bd, scale=c["scale"], causal=c["causal"], out=o, lse=lse)
+    return dict(fn=fn, work=flops, unit="TFLOP/s", bound="mfma", keep=(sets, kd, bd), cfg=c,
                 extra={"active_tiles_per_head": active, "partial_tiles_per_head": int((kinds == 2).sum()),
-                       "visible_fraction_of_active": round(visible / (active * 64 * 64), 4)})
+                       "visible_fraction_of_active": round(visible / (active * 64 * 64), 4),
+                       "buffer_sets": N_SETS_SMALL})
 
 
 def setup_bigbird(rf, torch, W):
@@ -407,32 +455,119 @@ SETUPS = {"copy": setup_copy, "bitmap": setup_bitmap, "layernorm": setup_layerno
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, on a bounded sample of the headline workload
+# CPU baseline: the oracle as it stands, on a bounded sample of each workload,
+# over the host's cores (one forked process per core, BLAS one thread each)
 # ---------------------------------------------------------------------------
 
-def cpu_baseline_softmax(W, budget_s=10.0):
-    """The fp64 oracle over the headline workload's rows, 64 rows at a time,
-    repeating whole passes until about budget_s of oracle time is spent."""
-    import oracle
-    c = W.CONFIGS["softmax"]
-    chunk = 64
-    rows = 0
-    spent = 0.0
-    cpu = 0.0
-    while spent < budget_s:
-        r0 = rows % c["rows"]
-        x = W.softmax_rows_input(c["seed"], chunk, c["cols"], row_ids=range(r0, r0 + chunk))
-        t0, p0 = time.perf_counter(), time.process_time()
-        oracle.softmax_rows(x)
-        spent += time.perf_counter() - t0
-        cpu += time.process_time() - p0
-        rows += chunk
-    gbs = 2 * rows * c["cols"] * 4 / spent / 1e9
-    cores = max(1, round(cpu / spent))   # threads the oracle kept busy (process CPU time / wall time)
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} rows x {c['cols']} cols ({rows / c['rows']:.2f} passes over the {c['rows']} rows; "
-                      f"fp64 NumPy three-pass softmax, {spent:.1f} s of oracle time, "
-                      f"{cpu / spent:.2f} CPU-s per s)"}
+def _cycle(items, n):
+    return [items[i % len(items)] for i in range(n)]
+
+
+def cpu_baseline_plan(name, W, workers):
+    """(task kind, tasks, algorithmic work of the tasks in the workload's unit
+    base, unit, sample description): each process gets a few tasks, about two
+    seconds of oracle work, and the work is counted as the GPU leg counts it."""
+    C, X = W.CONFIGS, W.EXTENSION_CONFIGS
+    if name in ("softmax", "layernorm"):
+        c = C["softmax"] if name == "softmax" else X["layernorm"]
+        per = 10 if name == "softmax" else 30
+        blocks = [(name, r, r + 64) for r in range(0, c["rows"], 64)]
+        tasks = _cycle(blocks, workers * per)
+        rows = 64 * len(tasks)
+        return (name, tasks, 2 * rows * c["cols"] * 4, "GB/s",
+                f"{rows} rows of {c['cols']} (64-row blocks, cycling over the {c['rows']} rows)")
+    if name in ("prefill", "sparse", "attn_f32"):
+        c = C[name]
+        if name == "prefill":
+            # one block of 1024 query rows per process, spread over heads and row ranges;
+            # work = 4 d flops per visible (row, key) pair, row i seeing i + 1 keys
+            blocks = [(name, b, h, r, r + 1024) for b in range(c["B"]) for h in range(c["H"])
+                      for r in range(0, c["Lq"], 1024)]
+            tasks = blocks[:workers]            # whole heads' row blocks, in order: an even mix
+            work = sum(4 * c["d"] * (r1 * (r1 + 1) - r0 * (r0 + 1)) / 2 for _, _, _, r0, r1 in tasks)
+            return ("attention", tasks, work, "TFLOP/s",
+                    f"{len(tasks)} blocks of 1024 query rows (of {len(blocks)} over the {c['B'] * c['H']} heads); "
+                    "work = the causal pairs of those rows")
+        if name == "attn_f32":
+            tasks = [(name, 0, 0, 0, c["Lq"])] * (workers * 1000)
+            return ("attention", tasks, len(tasks) * 4 * c["Lq"] * c["Lk"] * c["d"], "TFLOP/s",
+                    f"the whole workload (one head) {len(tasks)} times")
+        bm = W.config_block_mask(name)
+        blocks = [(name, b, h, r, r + 1024) for b in range(c["B"]) for h in range(c["H"])
+                  for r in range(0, c["Lq"], 1024)]
+        tasks = blocks[:workers * 4]
+        work = sum(4 * 64 ** 3 * int(bm[r0 // 64:r1 // 64].sum()) for _, _, _, r0, r1 in tasks)
+        return ("attention", tasks, work, "TFLOP/s",
+                f"{len(tasks)} blocks of 1024 query rows (of {len(blocks)} over the {c['B'] * c['H']} heads); "
+                "work = active 64x64 tiles in those rows")
+    if name == "decode":
+        c = C[name]
+        n = c["B"] * c["H"]
+        tasks = _cycle([(name, i, i + 8) for i in range(0, n, 8)], workers)
+        per_head = 2 * c["Lk"] * c["d"] * 2 + 2 * c["d"] * 2 + 4
+        return ("decode", tasks, 8 * len(tasks) * per_head, "GB/s",
+                f"{8 * len(tasks)} of the {n} heads, all {c['Lk']} keys each (unsplit)")
+    if name in ("bitmap", "bigbird"):
+        key = "bitmap" if name == "bitmap" else "bigbird_chunk"
+        c = X[key]
+        if name == "bitmap":
+            kinds, _ = W.extension_bitmap_mask()
+            blocks = [(key, "", b, h, r, r + 1024) for b in range(c["B"]) for h in range(c["H"])
+                      for r in range(0, c["Lq"], 1024)]
+            tasks = blocks[:workers * 4]
+            work = sum(4 * 64 ** 3 * int((kinds[t[4] // 64:t[5] // 64] != 0).sum()) for t in tasks)
+            return ("ext_attention", tasks, work, "TFLOP/s",
+                    f"{len(tasks)} blocks of 1024 query rows (of {len(blocks)}); "
+                    "work = active 64x64 tiles in those rows")
+        vis = W.bigbird_chunk_mask(c["seed"], c["Lq"], c["Lk"], c["n_global"], c["window"], c["n_random"])
+        kinds, _ = W.element_mask_tiles(vis)
+        keys = int(vis.any(axis=0).sum())
+        mask_bytes = kinds.size + 8 * c["Lq"] * int((kinds == 2).sum(axis=1).max(initial=0))
+        per_head = 2 * c["Lq"] * c["d"] * 2 + c["Lq"] * 4 + keys * 2 * c["d"] * 2 + mask_bytes / c["H"]
+        heads = [(key, "", 0, h, 0, c["Lq"]) for h in range(c["H"])]
+        tasks = _cycle(heads, workers * 8)
+        return ("ext_attention", tasks, per_head * len(tasks), "GB/s", f"{len(tasks)} heads (cycling over {c['H']})")
+    if name in ("alibi", "softcap", "window"):
+        c = X["score_mod"]
+        per = {"alibi": 2, "softcap": 1, "window": 2}[name]
+        heads = [("score_mod", name, b, h, 0, c["Lq"]) for b in range(c["B"]) for h in range(c["H"])]
+        tasks = _cycle(heads, workers * per)
+        L, Wn = c["Lq"], c["window"]
+        pairs = Wn * (Wn + 1) // 2 + (L - Wn) * Wn if name == "window" else L * L / 2
+        return ("ext_attention", tasks, 4 * pairs * c["d"] * len(tasks), "TFLOP/s",
+                f"{len(tasks)} of the {len(heads)} heads, every row")
+    if name in ("gqa", "mla"):
+        key = "gqa_decode" if name == "gqa" else "mla_decode"
+        c = X[key]
+        G = c["Hq"] // c["Hkv"]
+        units = [(key, b, j) for b in range(c["B"]) for j in range(c["Hkv"])]
+        tasks = _cycle(units, workers * (2 if name == "gqa" else 1))
+        per_unit = 2 * c["Lk"] * c["d"] * 2 + 2 * G * c["d"] * 2 + G * 4
+        return ("gqa", tasks, per_unit * len(tasks), "GB/s",
+                f"{len(tasks)} of the {len(units)} key/value heads, each with its {G} query heads")
+    if name == "moe":
+        c = X["moe"]
+        blocks = [("moe", t, t + 4096) for t in range(0, c["T"], 4096)]
+        tasks = _cycle(blocks, workers * 20)
+        return ("moe", tasks, len(tasks) * 4096 * (c["E"] * 4 + c["k"] * 8), "GB/s",
+                f"{4096 * len(tasks)} tokens (4096-token blocks, cycling over the {c['T']})")
+    return None
+
+
+def cpu_baseline(name, W):
+    """The fp64 oracle on a bounded sample of workload `name`, timed over the
+    host's cores, in the GPU leg's unit (the oracle is never tuned for this)."""
+    from oracle import pool
+    workers = pool.workers_available()
+    plan = cpu_baseline_plan(name, W, workers)
+    if plan is None:
+        return None
+    kind, tasks, work, unit, sample = plan
+    r = pool.timed_run(kind, tasks, workers)
+    scale = 1e9 if unit == "GB/s" else 1e12
+    return {"value": round(work / r["wall_s"] / scale, 6), "unit": unit, "cores": r["workers"], "kind": "oracle",
+            "sample": f"{sample}; fp64 NumPy oracle, {r['wall_s']:.2f} s wall on {r['workers']} processes "
+                      f"(BLAS one thread each; input drawing {r['input_gen_s']:.1f} s, not timed)"}
 
 
 def main():
@@ -442,6 +577,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workloads",
                     default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe,bigbird")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed calls of the first workload before any leg, so that no leg starts on an idle GPU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -458,32 +595,41 @@ def main():
         sys.exit(1)
 
     wanted = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    # Every leg's inputs go to the GPU first, so that the legs then run back to
+    # back: the GPU does not idle (and its clock does not drop) between them.
+    legs = {}
+    for name in wanted:
+        log(f"{name}: setup")
+        legs[name] = SETUPS[name](rf, torch, W)
+    settle_calls = settle(torch, legs[wanted[0]]["fn"], args.settle_ms)
+    log(f"settle: {settle_calls} untimed calls of {wanted[0]} ({args.settle_ms:g} ms)")
+
     results = {}
     cfgs = {}
     timer = Timer(torch)
     for name in wanted:
-        log(f"{name}: setup")
-        s = SETUPS[name](rf, torch, W)
+        s = legs[name]
         n_warm = warm_up(torch, s["fn"], args.warmup)
         log(f"{name}: timing {args.steps} calls (after {n_warm} warm-up calls)")
         call_ms, per, wall = timer.run(s["fn"], args.steps)
-        kern_ms = call_ms
-        merge_ms = None
-        if "subtract" in s:
-            warm_up(torch, s["subtract"], args.warmup)
-            merge_ms, _, _ = timer.run(s["subtract"], args.steps)
-            kern_ms = call_ms - merge_ms
         thr = s["work"] / (call_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
-        kthr = s["work"] / (kern_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
         peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS, "alu": FP32_VALU_PEAK_TFLOPS}[s["bound"]]
         r = {"workload": s["cfg"]["name"], "value": round(thr, 3), "unit": s["unit"],
              "ms_per_call": round(call_ms, 5), "ms_p10": round(float(np.percentile(per, 10)), 5),
              "ms_p90": round(float(np.percentile(per, 90)), 5), "wall_s": round(wall, 4),
-             "roofline": roofline(s["bound"], kthr, peak, s["unit"], measured_traffic(name)),
+             "roofline": roofline(s["bound"], thr, peak, s["unit"], measured_traffic(name)),
              "warmup_calls": n_warm}
-        if merge_ms is not None:
+        if "subtract" in s:
+            # The call is the partial kernel plus the merge; the roofline above
+            # is over the whole call. The partial kernel alone, labelled as such:
+            # the call time minus the merge timed on its own.
+            warm_up(torch, s["subtract"], args.warmup)
+            merge_ms = timer.run(s["subtract"], args.steps)[0]
+            kern_ms = call_ms - merge_ms
+            kthr = s["work"] / (kern_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
             r["merge_ms"] = round(merge_ms, 5)
-            r["partial_kernel_ms"] = round(kern_ms, 5)
+            r["partial_kernel_only"] = {"ms": round(kern_ms, 5), "achieved": round(kthr, 3),
+                                        "frac": round(kthr / peak, 4)}
         for alt, fn in s.get("alternatives", {}).items():
             warm_up(torch, fn, args.warmup)
             r[f"{alt}_ms"] = round(timer.run(fn, args.steps)[0], 5)
@@ -493,8 +639,16 @@ def main():
         results[name] = r
         cfgs[name] = s["cfg"]
         log(f"{name}: {r['value']} {r['unit']} ({call_ms:.4f} ms/call, frac {r['roofline']['frac']})")
-        del s
-        torch.cuda.empty_cache()
+    del legs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        for name in wanted:
+            log(f"{name}: cpu baseline (fp64 oracle on a sample, over the host's cores)")
+            cb = cpu_baseline(name, W)
+            if cb is not None:
+                results[name]["cpu_baseline"] = cb
 
     head = "softmax" if "softmax" in results else wanted[0]
     h = results[head]
@@ -507,11 +661,11 @@ def main():
         "config": {"workload": hc["name"], **{k: v for k, v in hc.items() if k in
                                               ("rows", "cols", "B", "H", "Lq", "Lk", "d", "num_splits")}},
         "roofline": h["roofline"],
+        "settle": {"workload": cfgs[wanted[0]]["name"], "ms": args.settle_ms, "calls": settle_calls},
         "workloads": results,
     }
-    if not args.no_cpu_baseline and head == "softmax":
-        log("cpu baseline: fp64 oracle on a sample of the softmax workload")
-        out["cpu_baseline"] = cpu_baseline_softmax(W)
+    if "cpu_baseline" in h:
+        out["cpu_baseline"] = h["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

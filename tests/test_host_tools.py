@@ -128,3 +128,25 @@ def test_source_sha_ignores_comments_but_not_code(tmp_path):
     assert changed != base
     (tmp_path / "h.h").write_text("int f() { return 2; }\n")
     assert traffic.source_sha("k.hip", str(tmp_path)) != changed
+
+
+def test_cpu_baseline_plan_covers_every_workload():
+    """Every benchmark workload (the calibration copy aside) has a bounded
+    oracle sample on the CPU, with its work in the leg's own unit."""
+    import bench
+    import workloads as W
+    for name in bench.SETUPS:
+        if name == "copy":
+            continue
+        kind, tasks, work, unit, sample = bench.cpu_baseline_plan(name, W, 4)
+        assert kind in ("attention", "decode", "softmax", "ext_attention", "layernorm", "gqa", "moe"), name
+        assert 4 <= len(tasks) <= 4 * 1000 and work > 0 and unit in ("GB/s", "TFLOP/s") and sample, name
+
+
+def test_cpu_baseline_prefill_work_is_the_causal_pairs():
+    import bench
+    import workloads as W
+    c = W.CONFIGS["prefill"]
+    _, tasks, work, _, _ = bench.cpu_baseline_plan("prefill", W, 4)
+    pairs = sum(sum(i + 1 for i in range(r0, r1)) for _, _, _, r0, r1 in tasks)
+    assert work == 4 * c["d"] * pairs
