@@ -49,6 +49,12 @@ def load():
     if not os.path.exists(path):
         raise RuntimeError(f"librf.so not found at {path}; build it with "
                            f"`python -m online_softmax_attention_pass_amd.build`")
+    # One HIP runtime per process: torch ships its own libamdhip64 and
+    # libhsa-runtime64, under the same sonames as the system's. Loaded first,
+    # torch's copies satisfy librf's dependencies by soname; loaded after
+    # librf, they would come in as a second runtime beside the system's, and
+    # librf's calls would then find no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {

@@ -486,3 +486,19 @@ def test_binding_rowwise_checks_outputs(case):
         k = _t(1, 2, 70, 64, dtype="f32")
     with pytest.raises(ValueError):
         rf.rf_attention_fwd_rowwise(q, k, k, **kw)
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loading librf through the binding before anything touches torch still
+    leaves ONE HIP runtime and one HSA runtime in the process (torch ships its
+    own copies under the system's sonames; two runtimes in one process make
+    librf's calls find no device)."""
+    import subprocess
+    import sys
+    code = ("import online_softmax_attention_pass_amd as rf; rf.load(); import torch; "
+            "maps = open('/proc/self/maps').read().split('\\n'); "
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l or 'libhsa-runtime64' in l}; "
+            "print(len([x for x in libs if 'amdhip64' in x]), len([x for x in libs if 'hsa-runtime64' in x]))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[-2:] == ["1", "1"], r.stdout
