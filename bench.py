@@ -20,12 +20,11 @@ prefill shape (B4 H32 L4096 d128): ALiBi bias, tanh softcap 50, and a
 tokens over 256 experts, top 8 (GB/s).
 
 Timing: every leg's inputs are made resident in HBM first; then, once,
-about 100 ms of untimed calls of the first leg (the GPU has idled while the
-host drew the inputs, and its clock needs that long to settle; reported as
-``settle``); then leg after leg, back to back: exactly W untimed warm-up
-calls, then K calls between one pair of HIP events recorded on the stream the
-kernels run on (the mean per call), then K more, each bracketed by its own
-events (the spread); device syncs bracket each region. No call finds its
+leg after leg, back to back: 50 ms of untimed calls while the clock settles
+after the change of load (reported per leg as ``settle``), then exactly W
+untimed warm-up calls, then K calls between one pair of HIP events recorded on
+the stream the kernels run on (the mean per call), then K more, each bracketed
+by its own events (the spread); device syncs bracket each region. No call finds its
 operands in the 256 MB Infinity Cache left by earlier calls: the softmax and
 layer-norm workloads (1 GiB per call) alternate two buffer sets, the
 block-sparse and bitmap workloads (about 135 MB) rotate three, the MoE and
@@ -120,7 +119,7 @@ class Timer:
         return mean_ms, per, wall
 
 
-SETTLE_MS = 100.0  # untimed GPU work before the first leg
+SETTLE_MS = 50.0  # untimed calls of each leg before its warm-up calls
 
 
 def warm_up(torch, fn, calls):
@@ -132,10 +131,12 @@ def warm_up(torch, fn, calls):
 
 
 def settle(torch, fn, ms):
-    """Untimed calls for `ms` milliseconds, once, before the first leg: the GPU
-    has idled while the host drew the inputs, and on this chip the first
-    milliseconds of steady calls after an idle period run slower while the
-    clock settles."""
+    """Untimed calls for `ms` milliseconds before a leg's warm-up calls. On this
+    chip the clock moves for several milliseconds after the load changes (from
+    idle, or from another leg's kind of work): a fresh run of causal-prefill
+    calls starts near 0.61 ms per call, slows to about 0.78 ms and comes back
+    to 0.60 ms over about 20 calls. Timing that transient would understate the
+    steady rate, so each leg first settles, and the record says how long."""
     n, t0 = 0, time.perf_counter()
     while (time.perf_counter() - t0) * 1e3 < ms:
         fn()
@@ -578,7 +579,7 @@ def main():
     ap.add_argument("--workloads",
                     default="softmax,prefill,decode,sparse,attn_f32,bitmap,layernorm,gqa,mla,alibi,softcap,window,moe,bigbird")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
-                    help="untimed calls of the first workload before any leg, so that no leg starts on an idle GPU")
+                    help="milliseconds of untimed calls of each leg before its --warmup calls (the clock settles)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -601,16 +602,15 @@ def main():
     for name in wanted:
         log(f"{name}: setup")
         legs[name] = SETUPS[name](rf, torch, W)
-    settle_calls = settle(torch, legs[wanted[0]]["fn"], args.settle_ms)
-    log(f"settle: {settle_calls} untimed calls of {wanted[0]} ({args.settle_ms:g} ms)")
 
     results = {}
     cfgs = {}
     timer = Timer(torch)
     for name in wanted:
         s = legs[name]
+        n_settle = settle(torch, s["fn"], args.settle_ms)
         n_warm = warm_up(torch, s["fn"], args.warmup)
-        log(f"{name}: timing {args.steps} calls (after {n_warm} warm-up calls)")
+        log(f"{name}: timing {args.steps} calls (after {n_settle} settle and {n_warm} warm-up calls)")
         call_ms, per, wall = timer.run(s["fn"], args.steps)
         thr = s["work"] / (call_ms * 1e-3) / (1e9 if s["unit"] == "GB/s" else 1e12)
         peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS, "alu": FP32_VALU_PEAK_TFLOPS}[s["bound"]]
@@ -618,7 +618,7 @@ def main():
              "ms_per_call": round(call_ms, 5), "ms_p10": round(float(np.percentile(per, 10)), 5),
              "ms_p90": round(float(np.percentile(per, 90)), 5), "wall_s": round(wall, 4),
              "roofline": roofline(s["bound"], thr, peak, s["unit"], measured_traffic(name)),
-             "warmup_calls": n_warm}
+             "warmup_calls": n_warm, "settle": {"ms": args.settle_ms, "calls": n_settle}}
         if "subtract" in s:
             # The call is the partial kernel plus the merge; the roofline above
             # is over the whole call. The partial kernel alone, labelled as such:
@@ -661,7 +661,7 @@ def main():
         "config": {"workload": hc["name"], **{k: v for k, v in hc.items() if k in
                                               ("rows", "cols", "B", "H", "Lq", "Lk", "d", "num_splits")}},
         "roofline": h["roofline"],
-        "settle": {"workload": cfgs[wanted[0]]["name"], "ms": args.settle_ms, "calls": settle_calls},
+        "settle_ms_per_leg": args.settle_ms,
         "workloads": results,
     }
     if "cpu_baseline" in h:
