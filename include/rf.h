@@ -284,6 +284,30 @@ int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, voi
                                 void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * rf_attention_decode_splitkv for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (without the workspace),
+ * same kernels, same result bit for bit. The partials live in a device array
+ * of the library's own, RF_DECODE_SCRATCH_BYTES (32 MiB) per GPU, held from
+ * the first call on that GPU until the process ends; it fits the partials of
+ * B*H*num_splits*(d + 1) fp32 values laid out as the workspace above (about
+ * 65,000 rows B*H*num_splits at d = 128; 2048 heads with 16 splits need 16.1 MiB).
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, or host threads) race and must be serialised by the
+ * caller. Nothing in the array needs clearing between calls: each call writes
+ * every partial it reads. The first call on a GPU looks the array's address up
+ * on that GPU; every call asks the stream for its device and launches the two
+ * kernels. No call allocates or frees memory.
+ * Errors: as rf_attention_decode_splitkv, and RF_ERR_WORKSPACE when the
+ * partials need more than RF_DECODE_SCRATCH_BYTES (checked before any HIP
+ * call).
+ */
+#define RF_DECODE_SCRATCH_BYTES (32u << 20)
+int rf_attention_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        int B, int H, int Lk, int d, float scale, int num_splits, int dtype,
+                                        void* stream);
+
+/*
  * Bytes of device workspace that rf_attention_decode_gqa needs: 0 when
  * num_splits == 1 (no partials), else B*Hq*num_splits*(d + 1) fp32 values laid
  * out and rounded as for rf_attention_decode_splitkv. Returns 0 for invalid
@@ -349,7 +373,7 @@ const char* rf_status_string(int status);
 const char* rf_last_error_message(void);
 
 /* ABI version of this header: bumped when a signature or semantic changes. */
-#define RF_ABI_VERSION 6
+#define RF_ABI_VERSION 7
 int rf_abi_version(void);
 
 #ifdef __cplusplus

@@ -17,7 +17,7 @@ import os
 __all__ = [
     "RF_F32", "RF_BF16", "RFError", "load", "library_path",
     "rf_softmax_rows", "rf_layernorm_rows", "rf_attention_fwd", "rf_attention_fwd_bitmap", "rf_attention_fwd_mod",
-    "rf_attention_decode_splitkv",
+    "rf_attention_decode_splitkv", "rf_attention_decode_splitkv_noalloc",
     "rf_attention_decode_splitkv_workspace_size", "rf_attention_decode_gqa", "rf_attention_decode_gqa_workspace_size",
     "rf_lse_merge", "rf_moe_route", "rf_attention_fwd_rowwise", "rf_attention_plan", "rf_abi_version",
 ]
@@ -65,6 +65,7 @@ def load():
         "rf_attention_fwd_mod": ([P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, F, I, P], I),
         "rf_attention_decode_splitkv_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_splitkv": ([P, P, P, P, P, I, I, I, I, F, I, P, SZ, I, P], I),
+        "rf_attention_decode_splitkv_noalloc": ([P, P, P, P, P, I, I, I, I, F, I, I, P], I),
         "rf_attention_decode_gqa_workspace_size": ([I, I, I, I], SZ),
         "rf_attention_decode_gqa": ([P, P, P, P, P, I, I, I, I, I, F, I, P, SZ, I, P], I),
         "rf_lse_merge": ([P, P, P, P, I64, I, I, I, P], I),
@@ -336,6 +337,34 @@ def rf_attention_decode_splitkv(q, k, v, scale=None, num_splits=16, workspace=No
                                          float(scale), num_splits, _ptr(workspace), nbytes, _dtype_code(q),
                                          _stream(dev))
     _check(st, "rf_attention_decode_splitkv")
+    return o, lse
+
+
+def rf_attention_decode_splitkv_noalloc(q, k, v, scale=None, num_splits=16, out=None, lse=None, want_lse=True):
+    """Split-KV decode with the partials in the library's own device scratch (no
+    workspace, nothing allocated by the library). Same result as
+    rf_attention_decode_splitkv. Calls that overlap on one GPU race."""
+    torch = _torch()
+    lib = load()
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, H, 1, d]")
+    B, H, _, d = q.shape
+    Lk = k.shape[2]
+    if k.shape != (B, H, Lk, d) or v.shape != (B, H, Lk, d):
+        raise ValueError("k, v must be [B, H, Lk, d] matching q")
+    _check_same_dtype(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    _check_out(o, q.shape, q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_out(lse, (B, H), torch.float32, "lse")
+    dev = _dev(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.rf_attention_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Lk, d,
+                                                 float(scale), num_splits, _dtype_code(q), _stream(dev))
+    _check(st, "rf_attention_decode_splitkv_noalloc")
     return o, lse
 
 

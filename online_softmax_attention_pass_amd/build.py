@@ -26,6 +26,7 @@ SOURCES = [
     "layernorm_rows.hip",
     "lse_merge.hip",
     "decode_splitkv.hip",
+    "decode_noalloc.hip",
     "attention_f32.hip",
     "attention_bf16.hip",
     "moe_route.hip",

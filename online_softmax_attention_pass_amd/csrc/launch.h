@@ -21,6 +21,14 @@ hipError_t launch_lse_merge(const float* o_parts, const float* lse_parts, void* 
 hipError_t launch_decode_partials(const void* q, const void* k, const void* v, float* o_parts,
                                   float* lse_parts, int B, int H, int Lk, int d, float scale,
                                   int num_splits, hipStream_t stream);
+// Split-KV decode with the partials in the library's own device scratch array
+// (no allocation, no workspace argument): partials, then the merge into o, lse.
+// The partial LSEs start lse_off bytes into the scratch; the caller has checked
+// that the layout fits in kDecodeScratchBytes.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_splitkv_scratch(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                         int H, int Lk, int d, float scale, int num_splits, size_t lse_off,
+                                         hipStream_t stream);
 // block_mask: NULL (dense) or tile kinds [ceil(Lq/64), ceil(Lk/64)]. tile_bits:
 // NULL (every nonzero kind is a full tile) or uint64 [same tiles, 64] row
 // bitmaps, used where the kind is neither 0 nor 1.

@@ -18,6 +18,8 @@
 
 namespace {
 
+static_assert(rf::kDecodeScratchBytes == RF_DECODE_SCRATCH_BYTES, "one scratch size on both sides of the ABI");
+
 thread_local std::string g_last_error;
 
 int fail(int status, const char* fmt, ...) {
@@ -391,39 +393,52 @@ size_t rf_attention_decode_splitkv_workspace_size(int B, int H, int d, int num_s
   return w.total;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the two split-KV decode entry points; on success
+// w holds the partials' layout. Returns RF_OK, or the failing status with its
+// message set. Makes no HIP call.
+int decode_args(const char* name, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int Lk, int d, float scale, int num_splits, int dtype, DecodeWs& w) {
+  if (dtype != RF_F32 && dtype != RF_BF16) return fail(RF_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+  if (B < 0 || H < 0 || Lk < 0)
+    return fail(RF_ERR_INVALID_ARG, "%s: negative size (B=%d H=%d Lk=%d)", name, B, H, Lk);
+  if (d < 1) return fail(RF_ERR_INVALID_ARG, "%s: d = %d < 1", name, d);
+  if (num_splits < 1 || num_splits > 1024)
+    return fail(RF_ERR_INVALID_ARG, "%s: num_splits = %d outside 1..1024", name, num_splits);
+  if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "%s: scale is not finite", name);
+  if (dtype != RF_BF16) return fail(RF_ERR_UNSUPPORTED, "%s: only bf16 is supported", name);
+  if (d != 64 && d != 128) return fail(RF_ERR_UNSUPPORTED, "%s: d must be 64 or 128, got %d", name, d);
+  int64_t nk = 1;
+  if (!mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, 2))
+    return fail(RF_ERR_INVALID_ARG, "%s: tensor size overflows int64", name);
+  if (!decode_ws_layout(B, H, d, num_splits, w)) return fail(RF_ERR_INVALID_ARG, "%s: workspace size overflows", name);
+  if (int64_t(B) * H == 0) return RF_OK;
+  if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "%s: NULL q or o", name);
+  if (Lk > 0 && (k == nullptr || v == nullptr)) return fail(RF_ERR_INVALID_ARG, "%s: NULL k or v", name);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
+    return fail(RF_ERR_UNSUPPORTED, "%s: needs 16-byte aligned q, k, v and 8-byte aligned o", name);
+  if (lse != nullptr && !aligned(lse, 4)) return fail(RF_ERR_INVALID_ARG, "%s: lse misaligned", name);
+  return RF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                 int Lk, int d, float scale, int num_splits, void* workspace,
                                 size_t workspace_bytes, int dtype, void* stream) {
+  const char* name = "rf_attention_decode_splitkv";
   try {
-    if (dtype != RF_F32 && dtype != RF_BF16)
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: unknown dtype %d", dtype);
-    if (B < 0 || H < 0 || Lk < 0)
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: negative size (B=%d H=%d Lk=%d)", B, H, Lk);
-    if (d < 1) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: d = %d < 1", d);
-    if (num_splits < 1 || num_splits > 1024)
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: num_splits = %d outside 1..1024", num_splits);
-    if (!std::isfinite(scale)) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: scale is not finite");
-    if (dtype != RF_BF16) return fail(RF_ERR_UNSUPPORTED, "rf_attention_decode_splitkv: only bf16 is supported");
-    if (d != 64 && d != 128)
-      return fail(RF_ERR_UNSUPPORTED, "rf_attention_decode_splitkv: d must be 64 or 128, got %d", d);
-    int64_t nk = 1;
-    if (!mul_ok(nk, B) || !mul_ok(nk, H) || !mul_ok(nk, Lk) || !mul_ok(nk, d) || !mul_ok(nk, 2))
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: tensor size overflows int64");
     DecodeWs w;
-    if (!decode_ws_layout(B, H, d, num_splits, w))
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: workspace size overflows");
+    const int st = decode_args(name, q, k, v, o, lse, B, H, Lk, d, scale, num_splits, dtype, w);
+    if (st != RF_OK) return st;
     if (int64_t(B) * H == 0) return ok();
-    if (q == nullptr || o == nullptr) return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: NULL q or o");
-    if (Lk > 0 && (k == nullptr || v == nullptr))
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: NULL k or v");
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 8))
-      return fail(RF_ERR_UNSUPPORTED,
-                  "rf_attention_decode_splitkv: needs 16-byte aligned q, k, v and 8-byte aligned o");
-    if (lse != nullptr && !aligned(lse, 4))
-      return fail(RF_ERR_INVALID_ARG, "rf_attention_decode_splitkv: lse misaligned");
     if (workspace == nullptr || workspace_bytes < w.total || !aligned(workspace, 256))
-      return fail(RF_ERR_WORKSPACE,
-                  "rf_attention_decode_splitkv: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)",
+      return fail(RF_ERR_WORKSPACE, "%s: workspace needs %zu bytes, 256-byte aligned (got %zu at %p)", name,
                   w.total, workspace_bytes, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* o_parts = static_cast<float*>(workspace);
@@ -433,9 +448,32 @@ int rf_attention_decode_splitkv(const void* q, const void* k, const void* v, voi
     e = rf::launch_lse_merge(o_parts, lse_parts, o, lse, int64_t(B) * H, num_splits, d, RF_BF16, s);
     return hip_status(e, "rf_attention_decode_splitkv (merge)");
   } catch (const std::exception& e) {
-    return fail(RF_ERR_HIP, "rf_attention_decode_splitkv: %s", e.what());
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
   } catch (...) {
-    return fail(RF_ERR_HIP, "rf_attention_decode_splitkv: unknown exception");
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
+  }
+}
+
+int rf_attention_decode_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                        int H, int Lk, int d, float scale, int num_splits, int dtype, void* stream) {
+  const char* name = "rf_attention_decode_splitkv_noalloc";
+  try {
+    DecodeWs w;
+    const int st = decode_args(name, q, k, v, o, lse, B, H, Lk, d, scale, num_splits, dtype, w);
+    if (st != RF_OK) return st;
+    if (int64_t(B) * H == 0) return ok();
+    if (w.total > rf::kDecodeScratchBytes)
+      return fail(RF_ERR_WORKSPACE,
+                  "%s: the partials of B*H*num_splits = %lld rows need %zu bytes, above the library's %zu-byte "
+                  "scratch; use rf_attention_decode_splitkv with a caller workspace",
+                  name, (long long)(int64_t(B) * H * num_splits), w.total, rf::kDecodeScratchBytes);
+    const hipError_t e = rf::launch_decode_splitkv_scratch(q, k, v, o, lse, B, H, Lk, d, scale, num_splits,
+                                                           w.lse_off, static_cast<hipStream_t>(stream));
+    return hip_status(e, name);
+  } catch (const std::exception& e) {
+    return fail(RF_ERR_HIP, "%s: %s", name, e.what());
+  } catch (...) {
+    return fail(RF_ERR_HIP, "%s: unknown exception", name);
   }
 }
 

@@ -48,7 +48,7 @@ def test_exports_no_cxx_names_for_the_abi(lib):
 
 
 def test_abi_version(lib):
-    assert lib.rf_abi_version() == 6
+    assert lib.rf_abi_version() == 7
 
 
 def test_status_strings(lib):
