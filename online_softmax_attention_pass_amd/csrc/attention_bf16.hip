@@ -166,7 +166,7 @@ struct ScoreMod {
 // tiles active for this wave's own mask row. The scan itself is scalar bit work.
 // ONE_ROW: the workgroup's rows are one mask row (64 query rows), so a wave's
 // own words are the workgroup's and are not kept twice.
-template <bool ONE_ROW>
+template <bool ONE_ROW, int MR>
 struct TileWalker {
   const uint8_t* mask;
   int n_mask_cols, mr0, mr1, mr_w, kt_end;
@@ -178,20 +178,37 @@ struct TileWalker {
   bool bits = false;
   uint64_t pv_bits = 0, pg_bits = 0;
 
-  __device__ void refill(int b) {
+  // This lane's mask bytes for tile b + lane, one per mask row of the
+  // workgroup (MR rows at most): unconditional loads of clamped (valid)
+  // addresses, without waiting for them; apply_kinds drops what the clamp
+  // stood in for.
+  __device__ void load_kinds(int b, uint32_t (&kinds)[MR]) const {
     const int kt = b + int(threadIdx.x & 63);
+    const int mc = min(kt * bn / kMaskTile, n_mask_cols - 1);
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const int mr = min(mr0 + i, ONE_ROW ? mr0 : mr1);
+      kinds[i] = mask[int64_t(mr) * n_mask_cols + mc];
+    }
+  }
+  __device__ void refill(int b) {
+    uint32_t kinds[MR];
+    load_kinds(b, kinds);
+    apply_kinds(b, kinds);
+  }
+  // The tile words of tiles b .. b + 63 from the lanes' mask bytes.
+  __device__ void apply_kinds(int b, const uint32_t (&kinds)[MR]) {
     bool any = false, mine = false, part = false, anypart = false;
-    if (kt < kt_end) {
-      const int mc = kt * bn / kMaskTile;
-      for (int mr = mr0; mr <= (ONE_ROW ? mr0 : mr1); ++mr) {
-        const uint8_t kind = mask[int64_t(mr) * n_mask_cols + mc];
-        const bool a = kind != 0;
-        const bool pa = bits && kind != 0 && kind != 1;
-        any |= a;
-        mine |= (ONE_ROW || mr == mr_w) && a;
-        anypart |= pa;
-        part |= (ONE_ROW || mr == mr_w) && pa;
-      }
+    const bool in_range = b + int(threadIdx.x & 63) < kt_end;
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      const uint32_t kind = (in_range && mr0 + i <= (ONE_ROW ? mr0 : mr1)) ? kinds[i] : 0u;
+      const bool a = kind != 0;
+      const bool pa = bits && kind != 0 && kind != 1;
+      any |= a;
+      mine |= (ONE_ROW || mr0 + i == mr_w) && a;
+      anypart |= pa;
+      part |= (ONE_ROW || mr0 + i == mr_w) && pa;
     }
     wg_bits = __builtin_amdgcn_ballot_w64(any);
     if (!ONE_ROW) wv_bits = __builtin_amdgcn_ballot_w64(mine);
@@ -398,23 +415,57 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int64_t lo_first = int64_t(q0) + off - mod.window + 1;
     const int kt_begin = SPLIT ? split * kt_split : ((MOD && mod.window > 0 && lo_first > 0) ? int(lo_first / BN) : 0);
     const int kt_end = SPLIT ? min(kt_all, kt_begin + kt_split) : kt_all;
-    TileWalker<BM == kMaskTile> walk{MASK ? block_mask : nullptr, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
-                    min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
+    TileWalker<BM == kMaskTile, (BM + kMaskTile - 1) / kMaskTile> walk{
+        MASK ? block_mask : nullptr, n_mask_cols, q0 / kMaskTile, min(q0 + BM - 1, Lq - 1) / kMaskTile,
+        min(q0w, Lq - 1) / kMaskTile, kt_end, BN};
     walk.bits = BITS;
+    // The item's first memory accesses go out together: the mask bytes of its
+    // first 64 key tiles, then its Q rows; only then is the mask read (to pick
+    // the first K and V tiles), and one wait before the first score product
+    // covers Q and those tiles: two memory latencies instead of three.
+    uint32_t kinds0[(BM + kMaskTile - 1) / kMaskTile];
+    const bool first_kinds = MASK && block_mask != nullptr && kt_begin < kt_end;
+    if (first_kinds) walk.load_kinds(kt_begin & ~63, kinds0);
 
     uint4 qf[KSTEPS];
-    {
+    if constexpr (MOD == 0) {
+      // The wave's 32 rows through a buffer resource that covers only them:
+      // rows past Lq read as zero, with no branch around each load.
+      const int n_rows = __builtin_amdgcn_readfirstlane(max(0, min(32, Lq - q0w)));
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(qh + int64_t(q0w) * D, uint32_t(n_rows) * D * 2);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        qf[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, (l32 * D + 16 * ks + 8 * h) * 2, 0, 0));
+    } else {
+      // (the score-modification instances keep plain loads and wait for them
+      // here: their register allocation is tight, and this keeps it spill-free)
       const int qi = q0w + l32;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
         uint4 x = make_uint4(0, 0, 0, 0);
         if (qi < Lq) x = *reinterpret_cast<const uint4*>(qh + int64_t(qi) * D + 16 * ks + 8 * h);
-        if (q_mode == 1) { x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u; }
-        if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
         qf[ks] = x;
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    if constexpr (MASK) __builtin_amdgcn_sched_barrier(0);  // the Q loads stay ahead of the wait for the mask bytes
+    if (first_kinds) {
+      // the bytes stay raw until here, so the first wait for them comes after the Q loads
+#pragma unroll
+      for (int i = 0; i < (BM + kMaskTile - 1) / kMaskTile; ++i) asm volatile("" : "+v"(kinds0[i]));
+      walk.apply_kinds(kt_begin & ~63, kinds0);
+    }
+    // A negative scale negates Q, a zero scale zeroes it (see score_coef);
+    // applied once the loads have landed.
+    auto q_modes = [&]() {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        uint4 x = qf[ks];
+        if (q_mode == 1) { x.x ^= 0x80008000u; x.y ^= 0x80008000u; x.z ^= 0x80008000u; x.w ^= 0x80008000u; }
+        if (q_mode == 2) x = make_uint4(0, 0, 0, 0);
+        qf[ks] = x;
+      }
+    };
 
     f32x16_t acc_o[DB];
 #pragma unroll
@@ -781,7 +832,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         dma_one(khead, head_bytes, kb1, uint32_t(tile(t1)) * BN * D * 2, kv_off, wave * IPW, IPW);
         load_bits(bb1, tile(t1), p1);
       }
-      publish_lds_loads();  // K(t0), K(t1), V(t0) resident
+      publish_lds_loads();  // Q, K(t0), K(t1), V(t0) resident
+      q_modes();
       score_mfmas(kb0, s0);
       mod_tile(s0, tile(t0));
       mask_tile(s0, tile(t0), m0, p0, row_word(p0, bb0));
