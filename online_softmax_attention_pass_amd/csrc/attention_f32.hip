@@ -229,6 +229,184 @@ __global__ __launch_bounds__(256) void attention_f32_kernel(const float* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small problems (d <= 64, too few 16-row tiles to occupy the chip): one
+// wavefront per query row. A workgroup's 4 waves are 4 consecutive rows of
+// one (b, h) and share each 64-key tile of K and V through LDS. In the score
+// step lane p takes key p of the tile (a d-long dot product against the
+// row's q, read as a broadcast); the row max and sum are wave reductions; in
+// the P.V step lane (g, c) accumulates output columns 4c .. 4c + 3 over key
+// group g of the tile (64 / (d/4) keys per group), and the key groups are
+// summed once, at the end. Per lane and tile this is about a quarter of the
+// 16-row kernel's instructions, on four times as many workgroups: the
+// single-head workload's 128 rows run as 32 workgroups instead of 8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float x) {
+  x = group_max<16>(x);
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return pair_max_halves(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16, 64);
+  return pair_sum_halves(x);
+}
+
+constexpr int kRowsPerWg = 4;
+
+template <int DMAX>
+__global__ __launch_bounds__(256) void attention_f32_rows_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
+    float* __restrict__ lse, int H, int Lq, int Lk, int d, float scale_log2, int causal,
+    const uint8_t* __restrict__ block_mask, const uint64_t* __restrict__ tile_bits, int n_rt, int64_t n_items,
+    int window, const float* __restrict__ slopes, float softcap) {
+  constexpr int BN = 64;           // keys per tile: one mask tile
+  constexpr int DP = DMAX + 4;     // padded LDS row: 16-byte aligned, rows 4 banks apart
+  constexpr int CG = DMAX / 4;     // P.V column groups of 4
+  constexpr int KG = 64 / CG;      // P.V key groups
+  constexpr int KPG = BN / KG;     // keys per key group
+  constexpr int PER = BN * DMAX / 256;  // K (and V) elements per thread and tile
+  static_assert(DMAX == 32 || DMAX == 64, "row kernel widths");
+  __shared__ __align__(16) float Ks[BN][DP];
+  __shared__ __align__(16) float Vs[BN][DP];
+  __shared__ __align__(16) float Qs[kRowsPerWg][DMAX];
+  __shared__ __align__(16) float Ps[kRowsPerWg][BN];
+
+  const int t = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int lane = t & 63;
+  const int cg = lane % CG, kg = lane / CG;
+  const int n_mask_cols = (Lk + kMaskTile - 1) / kMaskTile;
+  const int n_kt = (Lk + BN - 1) / BN;
+
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int64_t bh = item / n_rt;
+    const int q0 = int(item % n_rt) * kRowsPerWg;
+    const int qi = q0 + wave;  // this wave's query row
+    const float* qh = q + bh * int64_t(Lq) * d;
+    const float* kh = k + bh * int64_t(Lk) * d;
+    const float* vh = v + bh * int64_t(Lk) * d;
+    const int64_t qpos = int64_t(qi) + (Lk - Lq);
+    const float sl2 = slopes != nullptr ? slopes[bh % H] * kLog2e : 0.f;
+    const int64_t lo = window > 0 ? qpos - window + 1 : 0;
+    const int64_t lo_first = int64_t(q0) + (Lk - Lq) - window + 1;
+    const int64_t causal_last = int64_t(min(q0 + kRowsPerWg, Lq) - 1) + (Lk - Lq);
+    const int kt_stop = causal ? int(min(int64_t(n_kt), causal_last < 0 ? 0 : causal_last / BN + 1)) : n_kt;
+    auto visible = [&](int kt) {
+      const int k0 = kt * BN;
+      if (window > 0 && int64_t(k0) + BN - 1 < lo_first) return false;
+      return block_mask == nullptr || block_mask[int64_t(q0 / kMaskTile) * n_mask_cols + kt] != 0;
+    };
+    auto next_tile = [&](int kt) {
+      while (kt < kt_stop && !visible(kt)) ++kt;
+      return kt;
+    };
+    float kreg[PER], vreg[PER];
+    uint64_t wreg = ~uint64_t(0);
+    auto fetch = [&](int kt) {
+      const int k0 = kt * BN;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = t + 256 * j, c = i / DMAX, e = i % DMAX;
+        const bool in = (k0 + c < Lk) && e < d;
+        kreg[j] = in ? kh[int64_t(k0 + c) * d + e] : 0.f;
+        vreg[j] = in ? vh[int64_t(k0 + c) * d + e] : 0.f;
+      }
+      const int64_t tile = int64_t(q0 / kMaskTile) * n_mask_cols + kt;
+      const uint8_t kind = block_mask != nullptr ? block_mask[tile] : uint8_t(1);
+      wreg = ~uint64_t(0);
+      if (tile_bits != nullptr && kind != 1 && qi < Lq) wreg = tile_bits[tile * kMaskTile + (qi % kMaskTile)];
+    };
+
+    // q of this wave's row, zero past d and for rows past Lq
+    const float qv = (lane < DMAX && lane < d && qi < Lq) ? qh[int64_t(qi) * d + lane] : 0.f;
+    int kt = next_tile(0);
+    if (kt < kt_stop) fetch(kt);
+    __syncthreads();  // the previous item's readers of Qs are done
+    if (lane < DMAX) Qs[wave][lane] = qv;
+
+    float m = kNegInf, l = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    while (kt < kt_stop) {
+      const int k0 = kt * BN;
+      const uint64_t word = wreg;
+      __syncthreads();  // the previous tile's readers of Ks, Vs are done
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = t + 256 * j;
+        Ks[i / DMAX][i % DMAX] = kreg[j];
+        Vs[i / DMAX][i % DMAX] = vreg[j];
+      }
+      __syncthreads();
+      const int kt_next = next_tile(kt + 1);
+      if (kt_next < kt_stop) fetch(kt_next);
+
+      // score of key k0 + lane: four partial sums over 16-byte reads
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < DMAX; e += 4) {
+        const float4 qq = *reinterpret_cast<const float4*>(&Qs[wave][e]);
+        const float4 kk = *reinterpret_cast<const float4*>(&Ks[lane][e]);
+        ps[0] = fmaf(qq.x, kk.x, ps[0]);
+        ps[1] = fmaf(qq.y, kk.y, ps[1]);
+        ps[2] = fmaf(qq.z, kk.z, ps[2]);
+        ps[3] = fmaf(qq.w, kk.w, ps[3]);
+      }
+      const int kj = k0 + lane;
+      const bool vis = (kj < Lk) && (qi < Lq) && (!causal || int64_t(kj) <= qpos) && ((word >> lane) & 1) &&
+                       int64_t(kj) >= lo;
+      float t2 = ((ps[0] + ps[1]) + (ps[2] + ps[3])) * scale_log2;
+      if (softcap > 0.f) t2 = softcap * kLog2e * tanhf(t2 / (softcap * kLog2e));
+      t2 = fmaf(sl2, float(int64_t(kj) - qpos), t2);
+      const float sc = vis ? t2 : kNegInf;
+      const float mn = fmaxf(m, wave_max(sc));
+      const float mu = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m - mu);
+      const float pj = fast_exp2(sc - mu);
+      l = l * alpha + wave_sum(pj);
+      m = mn;
+      Ps[wave][lane] = pj;  // read back by this wave only (LDS operations of a wave stay in order)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < KPG; i += 4) {
+        const float4 pp = *reinterpret_cast<const float4*>(&Ps[wave][kg * KPG + i]);
+        const float pv[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 vv = *reinterpret_cast<const float4*>(&Vs[kg * KPG + i + u][4 * cg]);
+          acc[0] = fmaf(pv[u], vv.x, acc[0]);
+          acc[1] = fmaf(pv[u], vv.y, acc[1]);
+          acc[2] = fmaf(pv[u], vv.z, acc[2]);
+          acc[3] = fmaf(pv[u], vv.w, acc[3]);
+        }
+      }
+      kt = kt_next;
+    }
+    // sum the key groups (lanes cg, cg + CG, ...)
+#pragma unroll
+    for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], off, 64);
+    if (qi < Lq) {
+      const bool live = l > 0.f;
+      const float inv = live ? 1.f / l : 0.f;
+      float* orow = o + (bh * Lq + qi) * int64_t(d);
+      if (kg == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * cg + i < d) orow[4 * cg + i] = acc[i] * inv;
+      }
+      if (lse != nullptr && lane == 0) lse[bh * Lq + qi] = live ? (m + fast_log2(l)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// The row kernel takes a call when d <= 64 and the 16-row kernel would have
+// fewer workgroups than this (two per CU): there, latency, not throughput,
+// sets the time.
+constexpr int64_t kRowKernelBelow = 512;
+
 }  // namespace
 
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
@@ -239,6 +417,20 @@ hipError_t launch_attention_f32(const float* q, const float* k, const float* v, 
   const int64_t n_items = int64_t(B) * H * n_qt;
   const unsigned grid = unsigned(n_items < (1LL << 20) ? n_items : (1LL << 20));
   const float scale_log2 = float(double(scale) * 1.4426950408889634);
+  if (d <= 64 && n_items < kRowKernelBelow) {
+    const int n_rt = (Lq + kRowsPerWg - 1) / kRowsPerWg;
+    const int64_t n_row_items = int64_t(B) * H * n_rt;
+    const unsigned rgrid = unsigned(n_row_items < (1LL << 20) ? n_row_items : (1LL << 20));
+    if (d <= 32)
+      hipLaunchKernelGGL((attention_f32_rows_kernel<32>), dim3(rgrid), dim3(256), 0, stream, q, k, v, o, lse, H, Lq,
+                         Lk, d, scale_log2, causal, block_mask, tile_bits, n_rt, n_row_items, window, alibi_slopes,
+                         softcap);
+    else
+      hipLaunchKernelGGL((attention_f32_rows_kernel<64>), dim3(rgrid), dim3(256), 0, stream, q, k, v, o, lse, H, Lq,
+                         Lk, d, scale_log2, causal, block_mask, tile_bits, n_rt, n_row_items, window, alibi_slopes,
+                         softcap);
+    return hipGetLastError();
+  }
 #define RF_ATT_F32(DM)                                                                                    \
   hipLaunchKernelGGL((attention_f32_kernel<DM>), dim3(grid), dim3(256), 0, stream, q, k, v, o, lse, H, Lq, \
                      Lk, d, scale_log2, causal, block_mask, tile_bits, n_qt, n_items, window, alibi_slopes, \

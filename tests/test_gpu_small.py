@@ -198,6 +198,18 @@ def test_attention_f32(rf_gpu, d, B, H, Lq, Lk, causal, density):
     _check_attention(rf_gpu, "f32", d, B, H, Lq, Lk, causal, density, 106, 1e-5)
 
 
+# fp32 with d <= 64 runs on a one-row-per-wavefront kernel while the 16-row
+# kernel would have fewer than 512 workgroups; these shapes (512 and more
+# 16-row tiles) keep the 16-row kernel covered at small d as well.
+F32_TILED_CASES = [(2, 4, 1024, 300, True, None), (1, 8, 1100, 517, False, 0.5), (4, 2, 1030, 1030, True, 0.3)]
+
+
+@pytest.mark.parametrize("B,H,Lq,Lk,causal,density", F32_TILED_CASES)
+@pytest.mark.parametrize("d", [17, 64])
+def test_attention_f32_tiled_path_small_d(rf_gpu, d, B, H, Lq, Lk, causal, density):
+    _check_attention(rf_gpu, "f32", d, B, H, Lq, Lk, causal, density, 109, 1e-5)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_attention_scale_sign_and_zero(rf_gpu, dtype):
     for scale in (-0.3, 0.0, 2.5):
