@@ -9,7 +9,9 @@ one write per element); every workload that ran is also reported under
 ``workloads`` with its own time, throughput and roofline: causal bf16 prefill
 (B4 H32 L4096 d128, TFLOP/s), split-KV bf16 decode (B64 H32 Lk32768 d128, 16
 splits, GB/s), block-sparse bf16 attention (B2 H16 L8192 d64, TFLOP/s on
-active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds).
+active tiles) and single-head fp32 attention (B1 H1 L128 d64, microseconds;
+its few-microsecond calls are paced by the host's call rate in a plain loop,
+so the leg also times them captured in one HIP graph, ``graph_replay``).
 Extension workloads: element bitmaps in partial tiles (B2 H16 L8192 d64,
 TFLOP/s), row layer normalisation (fp32 4096 x 32768, GB/s), and decode with
 grouped queries at Lk 32768, d 128: 8 query heads per key/value head (B64 Hq64
@@ -145,6 +147,39 @@ def settle(torch, fn, ms):
             torch.cuda.synchronize()   # pace the host to the GPU so elapsed time is GPU time
     torch.cuda.synchronize()
     return n
+
+
+def graph_replay_ms(torch, fn, outputs, steps):
+    """Per-call GPU time of `steps` calls captured in one HIP graph and replayed:
+    a call of a few microseconds is otherwise paced by the host's call rate
+    (argument checks and the ctypes call take about 10 us in Python). The
+    replay's outputs must equal the eager call's."""
+    try:
+        fn()
+        torch.cuda.synchronize()
+        want = [t.clone() for t in outputs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # torch wants a non-default stream for capture
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        same = all(torch.equal(x, y) for x, y in zip(outputs, want))
+        return {"ms_per_call": round(a.elapsed_time(b) / steps, 5), "calls_per_replay": steps,
+                "outputs_equal_eager": bool(same)}
+    except Exception as e:  # noqa: BLE001 - a capture failure is reported, not fatal
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def roofline(bound, achieved, peak, unit, traffic):
@@ -437,7 +472,7 @@ def setup_attn_f32(rf, torch, W):
     lse = torch.empty((1, 1, 128), dtype=torch.float32, device="cuda")
     flops = 4 * 128 * 128 * 64
     return dict(fn=lambda: rf.rf_attention_fwd(q, k, v, scale=c["scale"], out=o, lse=lse), work=flops,
-                unit="TFLOP/s", bound="alu", keep=(q, k, v, o, lse), cfg=c)
+                unit="TFLOP/s", bound="alu", keep=(q, k, v, o, lse), cfg=c, graph=(o, lse))
 
 
 def setup_copy(rf, torch, W):
@@ -630,6 +665,8 @@ def main():
             r["merge_ms"] = round(merge_ms, 5)
             r["partial_kernel_only"] = {"ms": round(kern_ms, 5), "achieved": round(kthr, 3),
                                         "frac": round(kthr / peak, 4)}
+        if "graph" in s:
+            r["graph_replay"] = graph_replay_ms(torch, s["fn"], s["graph"], args.steps)
         for alt, fn in s.get("alternatives", {}).items():
             warm_up(torch, fn, args.warmup)
             r[f"{alt}_ms"] = round(timer.run(fn, args.steps)[0], 5)
