@@ -37,7 +37,9 @@ partial kernel plus the merge); the partial kernel alone is reported beside
 it, labelled.
 CPU baseline: after the GPU legs, the fp64 oracle as it stands, on a bounded
 sample of each workload, over all of this host's cores (one forked process
-per core, at most 16, BLAS one thread each), in each leg's own unit.
+per core, at most 16, BLAS one thread each), in each leg's own unit. A pilot
+pass over the sample sets how many times it is run, so that the timed part
+spends about 16 s of CPU time summed over the processes.
 """
 from __future__ import annotations
 
@@ -122,6 +124,7 @@ class Timer:
 
 
 SETTLE_MS = 50.0  # untimed calls of each leg before its warm-up calls
+CPU_BASELINE_CPU_S = 16.0  # CPU seconds (summed over the pool) of each leg's timed oracle sample
 
 
 def warm_up(torch, fn, calls):
@@ -501,8 +504,8 @@ def _cycle(items, n):
 
 def cpu_baseline_plan(name, W, workers):
     """(task kind, tasks, algorithmic work of the tasks in the workload's unit
-    base, unit, sample description): each process gets a few tasks, about two
-    seconds of oracle work, and the work is counted as the GPU leg counts it."""
+    base, unit, sample description): each process gets a few tasks, and the
+    work is counted as the GPU leg counts it."""
     C, X = W.CONFIGS, W.EXTENSION_CONFIGS
     if name in ("softmax", "layernorm"):
         c = C["softmax"] if name == "softmax" else X["layernorm"]
@@ -599,11 +602,17 @@ def cpu_baseline(name, W):
     if plan is None:
         return None
     kind, tasks, work, unit, sample = plan
-    r = pool.timed_run(kind, tasks, workers)
+    # A pilot pass sizes the timed run: the sample's tasks are run as many
+    # times as it takes to spend about CPU_BASELINE_CPU_S of CPU time.
+    pilot = pool.timed_run(kind, tasks, workers)
+    repeat = max(1, min(200, math.ceil(CPU_BASELINE_CPU_S / max(pilot["cpu_s"], 1e-3))))
+    r = pool.timed_run(kind, tasks, workers, repeat=repeat)
     scale = 1e9 if unit == "GB/s" else 1e12
-    return {"value": round(work / r["wall_s"] / scale, 6), "unit": unit, "cores": r["workers"], "kind": "oracle",
-            "sample": f"{sample}; fp64 NumPy oracle, {r['wall_s']:.2f} s wall on {r['workers']} processes "
-                      f"(BLAS one thread each; input drawing {r['input_gen_s']:.1f} s, not timed)"}
+    return {"value": round(work * repeat / r["wall_s"] / scale, 6), "unit": unit, "cores": r["workers"],
+            "kind": "oracle",
+            "sample": f"{sample}, run {repeat} times; fp64 NumPy oracle, {r['wall_s']:.2f} s wall and "
+                      f"{r['cpu_s']:.1f} s CPU on {r['workers']} processes (BLAS one thread each; input drawing "
+                      f"{r['input_gen_s']:.1f} s and a {pilot['wall_s']:.2f} s pilot pass, not timed)"}
 
 
 def main():

@@ -225,33 +225,36 @@ def map_tasks(kind: str, args_list, workers: int | None = None):
     return list(imap_tasks(kind, args_list, workers))
 
 
-def _timed_worker(kind, my_tasks, barrier, out_q, root):
+def _timed_worker(kind, my_tasks, repeat, barrier, out_q, root):
     _worker_init(root)
     prep, run = TASKS[kind]
     t_gen0 = time.perf_counter()
     inputs = [prep(*a) for a in my_tasks]
     t_gen = time.perf_counter() - t_gen0
     barrier.wait(timeout=900)                        # every worker starts the oracle together
+    c0 = time.process_time()
     t0 = time.perf_counter()
-    for x in inputs:
-        run(x)
+    for _ in range(repeat):
+        for x in inputs:
+            run(x)
     t1 = time.perf_counter()
-    out_q.put((t0, t1, t_gen))
+    out_q.put((t0, t1, t_gen, time.process_time() - c0))
 
 
-def timed_run(kind: str, args_list, workers: int | None = None) -> dict:
+def timed_run(kind: str, args_list, workers: int | None = None, repeat: int = 1) -> dict:
     """Time the oracle on the given tasks over `workers` processes (one process
     per core, BLAS one thread each). Every process first draws the inputs of
-    its share of the tasks; then all start together, and the wall clock runs
-    from that start to the last process's end (input drawing excluded, and
-    reported separately)."""
+    its share of the tasks; then all start together, run their share `repeat`
+    times, and the wall clock runs from that start to the last process's end
+    (input drawing excluded, and reported separately). `cpu_s` is the
+    processes' summed CPU time over the timed part."""
     workers = workers_available() if workers is None else workers
     workers = max(1, min(workers, len(args_list)))
     shares = [args_list[i::workers] for i in range(workers)]
     ctx = mp.get_context("fork")
     barrier = ctx.Barrier(workers)
     out_q = ctx.Queue()
-    procs = [ctx.Process(target=_timed_worker, args=(kind, [tuple(a) for a in s], barrier, out_q, _root()))
+    procs = [ctx.Process(target=_timed_worker, args=(kind, [tuple(a) for a in s], repeat, barrier, out_q, _root()))
              for s in shares]
     for p in procs:
         p.start()
@@ -262,4 +265,5 @@ def timed_run(kind: str, args_list, workers: int | None = None) -> dict:
             raise RuntimeError(f"oracle worker exited with {p.exitcode}")
     t0 = min(r[0] for r in res)
     t1 = max(r[1] for r in res)
-    return {"wall_s": t1 - t0, "workers": workers, "input_gen_s": max(r[2] for r in res), "tasks": len(args_list)}
+    return {"wall_s": t1 - t0, "workers": workers, "input_gen_s": max(r[2] for r in res), "tasks": len(args_list),
+            "repeat": repeat, "cpu_s": sum(r[3] for r in res)}

@@ -1207,7 +1207,9 @@ def test_pool_softmax_and_decode_equal_serial():
 def test_pool_timed_run_reports_workers():
     from oracle import pool
     r = pool.timed_run("attention", [("attn_f32", 0, 0, 0, 64), ("attn_f32", 0, 0, 64, 128)], workers=2)
-    assert r["workers"] == 2 and r["tasks"] == 2 and r["wall_s"] > 0
+    assert r["workers"] == 2 and r["tasks"] == 2 and r["wall_s"] > 0 and r["repeat"] == 1 and r["cpu_s"] > 0
+    r3 = pool.timed_run("attention", [("attn_f32", 0, 0, 0, 64), ("attn_f32", 0, 0, 64, 128)], workers=2, repeat=3)
+    assert r3["repeat"] == 3 and r3["cpu_s"] > r["cpu_s"]
 
 
 # ---------------------------------------------------------------------------
