@@ -1036,10 +1036,13 @@ hipError_t launch_attention_bf16_split(const void* q, const void* k, const void*
   // stream for issue slots.
   if (d == 128) {
 #if RF_SPLIT_SMALL_TILES
+    // The 1- and 2-wave workgroups take 64 KiB of LDS each, so at most one
+    // wave per SIMD is resident anyway; their register allocation is sized
+    // for one (the split epilogue does not fit two waves' 256 registers).
     if (Lq <= 32)
-      return launch_split<128, 1, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
+      return launch_split<128, 1, 1>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
     if (Lq <= 64)
-      return launch_split<128, 2, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
+      return launch_split<128, 2, 1>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale, n_splits, stream);
 #endif
     return launch_split<128, RF_ATT_NW_D128, RF_ATT_WPE_D128>(q, k, v, ws_o, ws_lse, n_heads, Lq, Lk, scale,
                                                                n_splits, stream);

@@ -38,7 +38,7 @@ KERNELS = {
     "bitmap": ("attention_bf16_sp_kernel<64, 2, 2, true, false, 0, true>", "attention_bf16.hip"),
     "decode": ("decode_partial_kernel", "decode_splitkv.hip"),
     "attn_f32": ("attention_f32", "attention_f32.hip"),
-    "gqa": ("attention_bf16_sp_kernel<128, 1, 2, false, true, 0, false>", "attention_bf16.hip"),
+    "gqa": ("attention_bf16_sp_kernel<128, 1, 1, false, true, 0, false>", "attention_bf16.hip"),
     "mla": ("attention_bf16_sp_kernel<128, 4, 2, false, true, 0, false>", "attention_bf16.hip"),
     "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),
     "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),

@@ -69,7 +69,7 @@ def test_traffic_keeps_shared_kernels_apart_by_run(tmp_path):
     decode (8 query heads per key/value head, 32-row tiles) and shared-cache
     decode (128-row tiles) use different instances."""
     copy = "vectorized_elementwise_kernel<MulFunctor>"
-    gqa_k, split = SP.format("128, 1, 2, false, true, 0, false"), SP.format("128, 4, 2, false, true, 0, false")
+    gqa_k, split = SP.format("128, 1, 1, false, true, 0, false"), SP.format("128, 4, 2, false, true, 0, false")
     mod1 = SP.format("128, 4, 2, false, false, 1, false")
     runs = []
     for r, (wl, kn, kf) in enumerate((("copy,gqa,alibi", gqa_k, 100.0), ("mla,window", split, 300.0))):
