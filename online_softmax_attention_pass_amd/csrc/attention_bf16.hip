@@ -967,6 +967,11 @@ hipError_t launch_sp_inst(const void* q, const void* k, const void* v, void* o, 
   const float c = score_coef(scale, &q_mode);
   const int64_t cap = 1LL << 22;
   const int xcd_remap = (n_items % 8 == 0 && n_items <= cap) ? 1 : 0;
+  // Causal items go in head groups (work_item). A masked call takes one head
+  // at a time: its items visit few tiles each, and with two heads the pair's
+  // K/V outgrows the L2 and is read about 1.3 times; with one, the traffic
+  // equals Q, K and V read once, at the same speed.
+  const int head_group = (causal && xcd_remap) ? (MASK ? 1 : RF_ATT_HEAD_GROUP) : 1;
   // Bytes of the row-bitmap array (validated below 2^32 at the boundary).
   const uint32_t bits_bytes =
       BITS ? uint32_t(int64_t((Lq + kMaskTile - 1) / kMaskTile) * ((Lk + kMaskTile - 1) / kMaskTile) * 512) : 0u;
@@ -975,7 +980,7 @@ hipError_t launch_sp_inst(const void* q, const void* k, const void* v, void* o, 
     hipLaunchKernelGGL((attention_bf16_sp_kernel<D, NW, WPE, BITS, false, MOD, MASK>), dim3(unsigned(n)), dim3(NW * 64),
                        0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, Lq, Lk, c, q_mode, causal,
-                       block_mask, n_qt, n, xcd_remap, (causal && xcd_remap) ? RF_ATT_HEAD_GROUP : 1, base,
+                       block_mask, n_qt, n, xcd_remap, head_group, base,
                        tile_bits, bits_bytes, 1, 0, nullptr, nullptr, mod);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
