@@ -273,13 +273,20 @@ __device__ __forceinline__ void dma_bits(const uint64_t* bits, uint32_t bytes, u
 }
 
 // One tensor's share of a tile: this wave's n direct-to-LDS instructions.
+// Each instruction's LDS destination (M0) is formed from one opaque base at
+// the point of use: otherwise the compiler keeps every (buffer, instruction)
+// destination of the loop in its own scalar register, and under pressure
+// spills them to vector lanes and reloads one before each load.
 __device__ __forceinline__ void dma_one(const uint16_t* head, uint32_t head_bytes, uint16_t* dst, uint32_t base,
                                         const uint32_t* lane_off, int ins0, int n) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, head_bytes);
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  uint32_t lds = uint32_t((uintptr_t)(lds_u8*)dst) + uint32_t(ins0) * 1024u;
+  asm volatile("" : "+s"(lds));
 #pragma unroll
   for (int j = 0; j < n; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (ins0 + j) * 512), 16,
-                                             base + lane_off[j], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(uintptr_t)(lds + j * 1024u),
+                                             16, base + lane_off[j], 0, 0, 0);
 }
 
 // Work item of launch slot gi. With xcd_remap, consecutive slots (which the
@@ -486,6 +493,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const int64_t lo_row = int64_t(qpos) - mod.window + 1;
     const int row_lo = (MOD && mod.window > 0) ? int(lo_row < 0 ? 0 : (lo_row > Lk ? Lk : lo_row)) : 0;
     const int64_t lo_wave = int64_t(q0w + 31) + off - mod.window + 1;
+    // The per-tile edge tests in 32 bits (one scalar each; the 64-bit forms
+    // took register pairs the masked walk could not spare): a causal tile
+    // needs the element mask when k0 > diag_edge, a window tile when
+    // k0 < lo_edge. Clamping keeps both tests exact for any k0 in [0, Lk).
+    auto clamp_i32 = [](int64_t x) { return int(x < INT32_MIN ? INT32_MIN : (x > INT32_MAX ? INT32_MAX : x)); };
+    const int diag_edge = clamp_i32(int64_t(q0w) + off - (BN - 1));
+    const int lo_edge = clamp_i32(lo_wave);
 
     // Key tile of walk position t: the walk runs first to last; with rev the
     // tiles are visited last to first (the diagonal first under an ALiBi
@@ -599,9 +613,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     auto mask_tile = [&](f32x16_t (&st)[MB], int kt, bool mine, int part, uint64_t word) {
       const int k0 = kt * BN;
       const bool bitmap = BITS && (part & 1);
-      const bool below_window = MOD && mod.window > 0 && int64_t(k0) < lo_wave;
-      const bool edge = !mine || bitmap || below_window ||
-                        (causal && int64_t(k0) + BN - 1 > int64_t(q0w) + off) || (k0 + BN > Lk);
+      const bool below_window = MOD && mod.window > 0 && k0 < lo_edge;
+      const bool edge = !mine || bitmap || below_window || (causal && k0 > diag_edge) || (k0 + BN > Lk);
       if (edge) {
         const int lim = mine ? row_lim - k0 - 4 * h : -BN;
         const int lo = row_lo - k0 - 4 * h;
