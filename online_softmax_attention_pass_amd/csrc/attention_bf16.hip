@@ -277,16 +277,20 @@ __device__ __forceinline__ void dma_bits(const uint64_t* bits, uint32_t bytes, u
 // the point of use: otherwise the compiler keeps every (buffer, instruction)
 // destination of the loop in its own scalar register, and under pressure
 // spills them to vector lanes and reloads one before each load.
+// The tile's first byte (base < head_bytes) becomes the resource's base, by
+// scalar arithmetic, so the lanes' offsets go in unchanged: no vector add per
+// instruction. The range still ends where the head does, so rows past the
+// last key read zero.
 __device__ __forceinline__ void dma_one(const uint16_t* head, uint32_t head_bytes, uint16_t* dst, uint32_t base,
                                         const uint32_t* lane_off, int ins0, int n) {
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(head, head_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(head) + base, head_bytes - base);
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   uint32_t lds = uint32_t((uintptr_t)(lds_u8*)dst) + uint32_t(ins0) * 1024u;
   asm volatile("" : "+s"(lds));
 #pragma unroll
   for (int j = 0; j < n; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(uintptr_t)(lds + j * 1024u),
-                                             16, base + lane_off[j], 0, 0, 0);
+                                             16, lane_off[j], 0, 0, 0);
 }
 
 // Work item of launch slot gi. With xcd_remap, consecutive slots (which the
