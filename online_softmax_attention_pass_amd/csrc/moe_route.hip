@@ -204,6 +204,144 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const T* __restrict__ lo
   }
 }
 
+// The same routing for 128 < E <= 256 (16 lanes per token, 16 logits per
+// lane) and k <= 16, with two changes that cut the vector work of the
+// selection by about half:
+//   - a lane reads its logits as 16-byte vectors: lane g holds the VE
+//     consecutive experts VE g .. VE g + VE - 1 of each 16 VE-expert block,
+//     so e(j) = (j / VE) 16 VE + VE g + j % VE, still increasing in j;
+//   - each lane sorts its own C best logits once (value, then lower expert
+//     first). A round then compares only the lanes' heads: the group maximum
+//     of the heads, the lowest expert holding it, and the winning lane moves
+//     to its next entry. A lane whose list runs out while it still holds
+//     logits not in it rebuilds the list from those (rare: it needs more than
+//     C of the token's k largest). The rounds use selects, not branches, so
+//     the lanes of a wave stay on one path. With C = 4 the routing of 256
+//     experts ran about 8% faster than the rescanning rounds above; with
+//     C = 3 the rebuilds cost more than the shorter lists saved.
+// The choice is the same as the rounds above: the largest remaining logit,
+// and among equal ones the lowest expert index.
+template <typename T, int C>
+__global__ __launch_bounds__(256) void moe_route_heads_kernel(const T* __restrict__ logits,
+                                                              int32_t* __restrict__ idx_out,
+                                                              float* __restrict__ w_out, int64_t T_, int E, int k,
+                                                              int renorm) {
+  constexpr int G = 16, EPL = 16, TPB = 256 / G;
+  constexpr int VE = 16 / int(sizeof(T));  // experts per 16-byte vector
+  constexpr int NV = EPL / VE;             // vectors per lane
+  const int g = threadIdx.x % G;
+  auto expert = [&](int j) { return (j / VE) * (16 * VE) + VE * g + j % VE; };
+  for (int64_t t0 = int64_t(blockIdx.x) * TPB; t0 < T_; t0 += int64_t(gridDim.x) * TPB) {
+    const int64_t t = t0 + threadIdx.x / G;
+    const bool live = t < T_;                   // uniform within a group
+    const T* row = logits + (live ? t : 0) * int64_t(E);
+    uint4 raw[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      // E is a multiple of VE, so a vector lies wholly inside the row or wholly
+      // past it; one past it reads the row's first vector and is set aside.
+      const int e0 = v * 16 * VE + VE * g;
+      raw[v] = nt_load(reinterpret_cast<const uint4*>(row + (e0 < E ? e0 : 0)));
+    }
+    float x[EPL];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e0 = v * 16 * VE + VE * g;
+      const bool in = live && e0 < E;
+      const uint32_t wd[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
+#pragma unroll
+      for (int c = 0; c < VE; ++c) {
+        float f;
+        if constexpr (sizeof(T) == 4) f = __uint_as_float(wd[c]);
+        else f = (c & 1) ? bf16_hi(wd[c / 2]) : bf16_lo(wd[c / 2]);
+        x[v * VE + c] = in ? f : kNegInf;
+      }
+    }
+    // softmax statistics of the token
+    float m = kNegInf;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) m = fmaxf(m, x[j]);
+    m = group_max_all<G>(m);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s += fast_exp2((x[j] - m) * kLog2e);
+    const float inv_l = 1.f / group_sum_all<G>(s);
+
+    uint32_t hk[EPL];  // ordered bits; 0 = absent
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) hk[j] = (live && expert(j) < E) ? ordered_bits(x[j]) : 0u;
+    // This lane's C best (value descending, equal values in slot order), over
+    // the slots not yet taken; n = how many of them it holds, more = whether
+    // it holds further logits beyond them.
+    uint32_t hv[C];
+    int hj[C];
+    int n = 0;
+    bool more = false;
+    uint32_t taken = 0;
+    auto build = [&]() {
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        hv[i] = 0u;
+        hj[i] = 0;
+      }
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const uint32_t v = ((taken >> j) & 1u) ? 0u : hk[j];
+        cnt += v != 0u;
+        // insert after every entry it does not exceed
+#pragma unroll
+        for (int i = C - 1; i >= 0; --i) {
+          const bool gt = v > hv[i];
+          const bool gt_prev = i == 0 ? true : v > hv[i - 1];
+          if (i > 0) {
+            hv[i] = gt_prev ? hv[i - 1] : (gt ? v : hv[i]);
+            hj[i] = gt_prev ? hj[i - 1] : (gt ? j : hj[i]);
+          } else {
+            hv[0] = gt ? v : hv[0];
+            hj[0] = gt ? j : hj[0];
+          }
+        }
+      }
+      n = cnt < C ? cnt : C;
+      more = cnt > C;
+    };
+    build();
+    float p_mine = 0.f;
+    int e_mine = 0;
+    float psum = 0.f;
+    for (int r = 0; r < k; ++r) {
+      // selects only (no branch per lane): every lane computes every value
+      const uint32_t mx = group_umax<G>(hv[0]);
+      const uint32_t eh = uint32_t(expert(hj[0]));
+      const bool top = n > 0 && hv[0] == mx;
+      const uint32_t ei = group_umin<G>(top ? eh : 0xFFFFFFFFu);
+      const bool win = top && eh == ei;
+      const float p = fast_exp2((from_ordered_bits(mx) - m) * kLog2e) * inv_l;
+      psum += p;
+      p_mine = g == r ? p : p_mine;
+      e_mine = g == r ? int(ei) : e_mine;
+      taken |= win ? 1u << hj[0] : 0u;
+#pragma unroll
+      for (int i = 0; i + 1 < C; ++i) {
+        hv[i] = win ? hv[i + 1] : hv[i];
+        hj[i] = win ? hj[i + 1] : hj[i];
+      }
+      hv[C - 1] = win ? 0u : hv[C - 1];
+      n -= win ? 1 : 0;
+      const bool refill = win && n == 0 && more;
+      if (__builtin_amdgcn_ballot_w64(refill)) {
+        if (refill) build();
+      }
+    }
+    const float scale = renorm ? 1.f / psum : 1.f;
+    if (live && g < k) {
+      idx_out[t * k + g] = e_mine;
+      w_out[t * k + g] = p_mine * scale;
+    }
+  }
+}
+
 template <typename T, int G, int EPL>
 hipError_t launch(const T* x, int32_t* idx, float* w, int64_t T_, int E, int k, int renorm, hipStream_t stream) {
   constexpr int TPB = 256 / G;
@@ -217,6 +355,14 @@ hipError_t launch(const T* x, int32_t* idx, float* w, int64_t T_, int E, int k, 
 // lanes (and cross-lane levels per selection round) that hold its E logits.
 template <typename T>
 hipError_t dispatch(const T* x, int32_t* idx, float* w, int64_t T_, int E, int k, int renorm, hipStream_t stream) {
+  constexpr int VE = 16 / int(sizeof(T));
+  if (E > 128 && E <= 256 && E % VE == 0 && k <= 16 && reinterpret_cast<uintptr_t>(x) % 16 == 0) {
+    constexpr int TPB = 256 / 16;
+    const int64_t blocks = (T_ + TPB - 1) / TPB;
+    const unsigned grid = unsigned(blocks < (1 << 20) ? blocks : (1 << 20));
+    hipLaunchKernelGGL((moe_route_heads_kernel<T, 4>), dim3(grid), dim3(256), 0, stream, x, idx, w, T_, E, k, renorm);
+    return hipGetLastError();
+  }
   if (E <= 1) return launch<T, 1, 1>(x, idx, w, T_, E, k, renorm, stream);
   if (E <= 2) return launch<T, 1, 2>(x, idx, w, T_, E, k, renorm, stream);
   if (E <= 4) return launch<T, 1, 4>(x, idx, w, T_, E, k, renorm, stream);

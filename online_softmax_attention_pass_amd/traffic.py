@@ -43,7 +43,7 @@ KERNELS = {
     "alibi": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),
     "window": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 1, false>", "attention_bf16.hip"),
     "softcap": ("attention_bf16_sp_kernel<128, 4, 2, false, false, 2, false>", "attention_bf16.hip"),
-    "moe": ("moe_route_kernel", "moe_route.hip"),
+    "moe": ("moe_route_heads_kernel", "moe_route.hip"),
     "bigbird": ("attention_rowwise_kernel", "attention_rowwise.hip"),
 }
 COPY_KEY = "MulFunctor"

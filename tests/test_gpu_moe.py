@@ -72,3 +72,18 @@ def test_moe_route_is_deterministic(rf_gpu):
     b = rf_gpu.rf_moe_route(xd, 8, True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [8, 16])
+def test_moe_route_top_experts_in_one_block(rf_gpu, dtype, k):
+    """The k largest logits sit in one contiguous block of 16 experts, then in a
+    block of experts 64 apart: each lane group that holds them must give up
+    more of them than it keeps sorted at once (the rebuild path of E <= 256)."""
+    x = W.moe_logits(175, 600, 256)
+    x[:300, :16] += np.float32(20.0)
+    x[300:, ::64] += np.float32(20.0)
+    x[300:, 1::64] += np.float32(19.0)
+    x[300:, 2::64] += np.float32(18.0)
+    x[300:, 3::64] += np.float32(17.0)
+    _check(rf_gpu, x, k, True, dtype, "one block")
