@@ -49,6 +49,9 @@ GQA_CASES = [  # B, Hq, Hkv, Lk, d, S
     (1, 12, 4, 64, 64, 1),         # exactly one tile, written directly
     (2, 24, 3, 2049, 128, 1),      # G = 8, no split
     (1, 32, 1, 1500, 128, 3),      # G = 32: one full 32-row tile
+    (2, 16, 8, 777, 128, 5),       # G = 2
+    (1, 16, 2, 999, 64, 3),        # G = 8 at d = 64
+    (2, 16, 4, 5000, 64, 6),       # G = 4 at d = 64
     (1, 66, 2, 1100, 128, 4),      # G = 33: a 64-row tile, ragged
     (1, 64, 1, 900, 128, 2),       # G = 64: one full 64-row tile
     (1, 65, 1, 700, 128, 3),       # G = 65: a 128-row tile
