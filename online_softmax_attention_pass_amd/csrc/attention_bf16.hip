@@ -432,6 +432,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const uint16_t* qh = q + bh * int64_t(Lq) * D;
     const uint16_t* khead = k + bh * int64_t(Lk) * D;
     const uint16_t* vhead = v + bh * int64_t(Lk) * D;
+    // Output addresses of this wave's rows. The masked instances form them
+    // here and hold them in VGPRs until the epilogue: as scalars they stayed
+    // live across the tile walk and took its spill slots. The others form
+    // them in the epilogue.
+    uint16_t* obase_m = nullptr;
+    float* lse_m = nullptr;
+    int rows_m = 0;
+    if constexpr (MASK && !SPLIT) {
+      obase_m = o + (bh * Lq + q0w) * int64_t(D);
+      lse_m = lse != nullptr ? lse + bh * Lq + q0w : nullptr;
+      rows_m = Lq - q0w;
+      asm volatile("" : "+v"(obase_m), "+v"(lse_m), "+v"(rows_m));
+    }
 
     int64_t last_key = int64_t(min(q0 + BM, Lq) - 1) + (causal ? off : int64_t(Lk));
     if (last_key > Lk - 1) last_key = Lk - 1;
@@ -957,17 +970,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           *reinterpret_cast<uint4*>(stage + l32 * D + 8 * (c ^ (l32 & (OCH - 1)))) =
               make_uint4(sx[0], sy[0], sx[1], sy[1]);
         }
-      uint16_t* obase = o + (bh * Lq + q0w) * int64_t(D);
+      uint16_t* obase = MASK ? obase_m : o + (bh * Lq + q0w) * int64_t(D);
 #pragma unroll
       for (int i = 0; i < 32 * OCH / 64; ++i) {
         const int g = 64 * i + lane, row = g / OCH, c = g % OCH;
         const uint4 x = *reinterpret_cast<const uint4*>(stage + row * D + 8 * (c ^ (row & (OCH - 1))));
         // O is written once: non-temporal stores keep the L2 for K and V
         // (0.3-0.8% on prefill and block-sparse; non-temporal Q loads lost 1%)
-        if (q0w + row < Lq) nt_store(x, reinterpret_cast<uint4*>(obase + row * D + 8 * c));
+        if (MASK ? row < rows_m : q0w + row < Lq) nt_store(x, reinterpret_cast<uint4*>(obase + row * D + 8 * c));
       }
     }
-    if (lse != nullptr && h == 0 && qi < Lq) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    if constexpr (MASK) {
+      if (lse_m != nullptr && h == 0 && l32 < rows_m) lse_m[l32] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    } else {
+      if (lse != nullptr && h == 0 && qi < Lq) lse[bh * Lq + qi] = live ? (m_ref + fast_log2(l_tot)) * kLn2 : kNegInf;
+    }
     }
   }
 }
