@@ -26,7 +26,7 @@ leg after leg, back to back: 50 ms of untimed calls while the clock settles
 after the change of load (reported per leg as ``settle``), then exactly W
 untimed warm-up calls, then K calls between one pair of HIP events recorded on
 the stream the kernels run on (the mean per call), then K more, each bracketed
-by its own events (the spread); device syncs bracket each region. No call finds its
+by its own events (their median, p10 and p90); device syncs bracket each region. No call finds its
 operands in the 256 MB Infinity Cache left by earlier calls: the softmax and
 layer-norm workloads (1 GiB per call) alternate two buffer sets, the
 block-sparse and bitmap workloads (about 135 MB) rotate three, the MoE and
@@ -660,6 +660,7 @@ def main():
         peak = {"hbm": HBM_PEAK_GBS, "mfma": BF16_PEAK_TFLOPS, "alu": FP32_VALU_PEAK_TFLOPS}[s["bound"]]
         r = {"workload": s["cfg"]["name"], "value": round(thr, 3), "unit": s["unit"],
              "ms_per_call": round(call_ms, 5), "ms_p10": round(float(np.percentile(per, 10)), 5),
+             "ms_median": round(float(np.median(per)), 5),
              "ms_p90": round(float(np.percentile(per, 90)), 5), "wall_s": round(wall, 4),
              "roofline": roofline(s["bound"], thr, peak, s["unit"], measured_traffic(name)),
              "warmup_calls": n_warm, "settle": {"ms": args.settle_ms, "calls": n_settle}}
