@@ -105,6 +105,7 @@ def _dtype_code(t) -> int:
 
 
 def _dev(*ts):
+    """The index of the one GPU all given tensors are on (None entries are skipped)."""
     dev = None
     for t in ts:
         if t is None:
@@ -113,20 +114,32 @@ def _dev(*ts):
             raise ValueError("all tensors must be on the GPU")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
+        i = t.get_device()
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
+            dev = i
+        elif i != dev:
             raise ValueError("all tensors must be on one device")
     return dev
 
 
-def _stream(dev):
-    return ctypes.c_void_p(_torch().cuda.current_stream(dev).cuda_stream)
+_raw_stream = None
+
+
+def _stream(dev: int):
+    """torch's current stream on device index dev, as the raw hipStream_t value.
+    (The raw query skips building a Stream object: small calls are paced by this
+    host path.)"""
+    global _raw_stream
+    if _raw_stream is None:
+        torch = _torch()
+        _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+            (lambda i: torch.cuda.current_stream(i).cuda_stream)
+    return _raw_stream(dev)
 
 
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0) if t is not None \
-        else ctypes.c_void_p(0)
+    """Device address of a tensor's data, or None (NULL) for a missing or empty tensor."""
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
 
 
 def _check_out(o, shape, dtype, what="out"):
