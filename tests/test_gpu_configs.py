@@ -170,6 +170,37 @@ def test_attention_bf16_long_keys(rf_gpu, d):
     _report(f"long keys d{d}", e_o, e_l, ref_o)
 
 
+def test_attention_and_decode_at_the_size_limit(rf_gpu):
+    """The largest key range the boundary accepts at d = 128 (Lk d 2 just below
+    2^31 bytes per head, 8,388,607 keys): a causal 64-row prefill (one
+    workgroup sweeps every key tile) and a 64-way split-KV decode over the same
+    K and V. Sampled prefill rows and the whole decode against the oracle."""
+    d = 128
+    Lk = (1 << 31) // (d * 2) - 1
+    assert Lk * d * 2 < (1 << 31)
+    note(f"size limit d={d} Lk={Lk}")
+    k = W.normal_tensor(122, W.TID_K, 1, 1, Lk, d, "bf16")
+    v = W.normal_tensor(122, W.TID_V, 1, 1, Lk, d, "bf16")
+    qa = W.normal_tensor(122, W.TID_Q, 1, 1, 64, d, "bf16")
+    qd = W.normal_tensor(123, W.TID_Q, 1, 1, 1, d, "bf16")
+    scale = 1 / math.sqrt(d)
+    kd, vd = dev_bf16(k), dev_bf16(v)
+    o, lse = rf_gpu.rf_attention_fwd(dev_bf16(qa), kd, vd, scale=scale, causal=True)
+    od, lsed = rf_gpu.rf_attention_decode_splitkv(dev_bf16(qd), kd, vd, scale=scale, num_splits=64)
+    del kd, vd
+    k64, v64 = O.bf16_bits_to_f64(k), O.bf16_bits_to_f64(v)
+    del k, v
+    rows = [0, 31, 32, 63]
+    ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(qa), k64, v64, scale, True, q_rows=rows)
+    e_o = assert_close(host_f64(o)[:, :, rows], ref_o, 1e-2, "size-limit prefill O")
+    e_l = assert_close(host_f64(lse)[:, :, rows], ref_lse, 1e-3, "size-limit prefill LSE")
+    _report("size limit prefill d128", e_o, e_l, ref_o)
+    ref_o, ref_lse = O.attention(O.bf16_bits_to_f64(qd), k64, v64, scale)
+    e_o = assert_close(host_f64(od), ref_o, 1e-2, "size-limit decode O")
+    e_l = assert_close(host_f64(lsed), ref_lse[:, :, 0], 1e-3, "size-limit decode LSE")
+    _report("size limit decode d128", e_o, e_l, ref_o)
+
+
 def test_decode_long_keys(rf_gpu):
     """2,000,003 keys split 61 ways (ragged last split), checked whole."""
     B, H, Lk, d, S = 1, 1, 2_000_003, 128, 61
