@@ -393,3 +393,33 @@ def test_softmax_ragged_even_widths_bf16(rf_gpu, cols):
     y = host_f64(rf_gpu.rf_softmax_rows(dev_bf16(x)))
     ref = O.softmax_rows(O.bf16_bits_to_f64(x))
     assert_close(y, ref, 1e-2, f"y cols={cols}")
+
+
+# ---------------------------------------------------------------------------
+# streams: every call is enqueued on torch's current stream
+# ---------------------------------------------------------------------------
+
+def test_calls_run_on_the_current_stream(rf_gpu):
+    """Under a side stream, the calls' results are complete once that stream
+    alone is synchronised, while the default stream is still busy with a spin
+    kernel queued before them: they were enqueued on the side stream."""
+    import torch
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep is not available")
+    q, k, v = (_normal(131, t, (1, 2, 300, 128), "bf16") for t in (0, 1, 2))
+    x = _normal(132, 3, (64, 5000), "f32")
+    qd, kd, vd, xd = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f32(x)
+    ref_o, ref_l = rf_gpu.rf_attention_fwd(qd, kd, vd, causal=True)
+    ref_y = rf_gpu.rf_softmax_rows(xd)
+    torch.cuda.synchronize()
+    o, l, y = torch.empty_like(ref_o), torch.empty_like(ref_l), torch.empty_like(ref_y)
+    side = torch.cuda.Stream()
+    note("attention and softmax on a side stream behind a busy default stream")
+    torch.cuda._sleep(200_000_000)          # about 0.1 s of spinning on the default stream
+    with torch.cuda.stream(side):
+        rf_gpu.rf_attention_fwd(qd, kd, vd, causal=True, out=o, lse=l)
+        rf_gpu.rf_softmax_rows(xd, out=y)
+    side.synchronize()
+    assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16))
+    assert torch.equal(l, ref_l) and torch.equal(y, ref_y)
+    torch.cuda.synchronize()
